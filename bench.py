@@ -1,0 +1,197 @@
+"""Benchmark of DiT dense joint attention on one MI355X.
+
+A step is one attention forward over one batch of synthetic inputs: for the
+default workload, B=1, H=24, N=16896 (512 text + 128x128 image tokens),
+d=128, bf16 in and out. Inputs are resident in HBM before timing starts.
+
+Prints ONE JSON line. ``value`` is TFLOP/s by 4*B*H*N^2*d over the wall
+clock of K back-to-back steps (synchronised on both sides). ``roofline``
+uses the per-launch kernel time from events recorded on the stream the
+kernel runs on. ``cpu_baseline`` times the fp64 CPU oracle on a bounded
+sample of query rows of the same workload (each output row depends on one
+query row, so a row sample is the same computation, only fewer rows).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "DiT attention fwd TFLOP/s at 16896-token shape; % of MI355X MFMA peak"
+PEAK_TFLOPS = {"bf16": 2516.6, "fp8": 5033.2}     # MI355X dense MFMA, 2.4 GHz
+HBM_PEAK_GBS = 8000.0
+KERNEL_SOURCES = ["attn_common.h", "attn_fwd_bf16.h", "attn_fwd_fp8.h", "dit_attn.hip"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "diffusion_transformer_attention_non_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kind: str, workload: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
+    taken on the current kernel sources; otherwise None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kind}_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("source_hash") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def time_launches(fn, warmup: int, steps: int):
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for a, b in evs:
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = [a.elapsed_time(b) for a, b in evs]
+    return wall, per
+
+
+def cpu_baseline(q, k, v, scale, budget_s: float):
+    """Time the fp64 oracle on a bounded row sample; return its TFLOP/s."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"),
+                      default=1)
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    B, H, N, d = q.shape
+    q64, k64, v64 = (t[:1].double().numpy() for t in (q, k, v))
+    # calibrate on 64 rows of every head of batch entry 0, then size the sample to the budget
+    rows = np.arange(64)
+    t0 = time.perf_counter()
+    oracle.attention(q64, k64, v64, scale, rows=rows)
+    t_cal = time.perf_counter() - t0
+    n_rows = int(min(N, max(64, 64 * budget_s / max(t_cal, 1e-3))))
+    rows = np.linspace(0, N - 1, n_rows).astype(np.int64)
+    t0 = time.perf_counter()
+    oracle.attention(q64, k64, v64, scale, rows=rows)
+    t = time.perf_counter() - t0
+    flops = 4.0 * H * n_rows * N * d
+    cpu = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"fp64 numpy oracle on {n_rows} of {N} query rows x {H} heads of batch entry 0 "
+                      f"({flops / 1e9:.1f} GFLOP in {t:.1f} s); host CPU: {cpu}"}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="t2i_2048")
+    ap.add_argument("--no-fp8", action="store_true", help="skip the fp8-e4m3 companion measurement")
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this library has no multi-GPU path "
+              "(every (b, h) slice is independent; sharding is described in DESIGN.md). "
+              "Run with --gpus 1.", file=sys.stderr)
+        return 2
+
+    import torch
+    import diffusion_transformer_attention_non_amd as dit
+    from workloads import WORKLOADS, make_qkv
+
+    w = WORKLOADS[args.workload]
+    scale = 1.0 / math.sqrt(w.d)
+    dev = torch.device("cuda:0")
+    q, k, v = make_qkv(w)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    od = torch.empty_like(qd)
+    stream = torch.cuda.current_stream()
+    handle = stream.cuda_stream
+    B, H, N, d = w.B, w.H, w.N, w.d
+
+    def step():
+        st = dit.dit_attn_fwd(qd, kd, vd, od, B, H, N, d, scale, dit.DIT_ATTN_BF16, handle)
+        if st != 0:
+            raise dit.DitAttnError(st, "dit_attn_fwd")
+
+    wall, per = time_launches(step, args.warmup, args.steps)
+    flops = w.flops
+    ms_per_step = wall / args.steps * 1e3
+    value = flops / (wall / args.steps) / 1e12
+    k_mean = statistics.fmean(per)
+    achieved = flops / (k_mean * 1e-3) / 1e12
+    peak = PEAK_TFLOPS["bf16"]
+    traffic = load_traffic("attn_fwd_bf16", w.name)
+    line = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic: Q, K, V iid N(0,1) rounded to bf16, seed 0",
+        "config": {"workload": w.name, "B": B, "H": H, "N": N, "d": d, "n_text": w.n_text,
+                   "n_image": w.n_image, "causal": False, "scale": scale},
+        "pct_of_peak": round(100.0 * value / peak, 2),
+        "kernel_ms": {"mean": round(k_mean, 4), "median": round(statistics.median(per), 4),
+                      "p95": round(sorted(per)[int(0.95 * (len(per) - 1))], 4), "min": round(min(per), 4)},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(achieved / peak, 4), "traffic": traffic},
+    }
+
+    if not args.no_fp8:
+        q8, dsq = dit.quantize_e4m3(qd)
+        k8, dsk = dit.quantize_e4m3(kd)
+        v8, dsv = dit.quantize_e4m3(vd)
+        descale = torch.cat([dsq, dsk, dsv]).contiguous()
+
+        def step8():
+            st = dit.dit_attn_fwd_ex(q8, k8, v8, od, B, H, N, d, scale, dit.DIT_ATTN_FP8_E4M3, descale, None,
+                                     handle)
+            if st != 0:
+                raise dit.DitAttnError(st, "dit_attn_fwd_ex")
+
+        wall8, per8 = time_launches(step8, args.warmup, args.steps)
+        v8_tflops = flops / (wall8 / args.steps) / 1e12
+        k8_mean = statistics.fmean(per8)
+        line["fp8"] = {"workload": w.name + "_fp8", "value": round(v8_tflops, 2), "unit": "TFLOP/s",
+                       "ms_per_step": round(wall8 / args.steps * 1e3, 4),
+                       "pct_of_fp8_peak": round(100.0 * v8_tflops / PEAK_TFLOPS["fp8"], 2),
+                       "roofline": {"bound": "mfma", "achieved": round(flops / (k8_mean * 1e-3) / 1e12, 2),
+                                    "peak": PEAK_TFLOPS["fp8"], "unit": "TFLOP/s",
+                                    "frac": round(flops / (k8_mean * 1e-3) / 1e12 / PEAK_TFLOPS["fp8"], 4),
+                                    "traffic": load_traffic("attn_fwd_fp8", w.name)}}
+
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(q, k, v, scale, args.cpu_budget)
+    line["context"] = ("pages (NVIDIA B200, FLUX 3 Image Klein, 2048x2048): Base text-to-image denoise "
+                       "14.24 s of 14.70 s; dense BF16 attention ~60% of DiT kernel time")
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

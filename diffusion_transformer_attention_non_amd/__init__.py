@@ -1,0 +1,94 @@
+"""MI355X (gfx950) dense joint text+image attention for diffusion transformers.
+
+O = softmax(Q K^T * scale) V over the concatenated text and image tokens,
+non-causal, computed by hand-written HIP kernels behind the C ABI of
+``libditattn.so`` (declared in ``include/dit_attn.h``). The functions below
+check torch tensors and pass their device addresses and the current stream
+to the C entry points; PyTorch only provides device memory and streams.
+"""
+from __future__ import annotations
+
+import math
+
+from . import _lib
+from ._lib import (DIT_ATTN_BF16, DIT_ATTN_EDEVICE, DIT_ATTN_EINVAL, DIT_ATTN_ELAUNCH, DIT_ATTN_FP8_E4M3,
+                   DIT_ATTN_OK, DIT_ATTN_EUNSUPPORTED, dit_attn_fwd, dit_attn_fwd_ex, dit_attn_quantize_e4m3,
+                   dit_attn_strerror, dit_attn_version)
+
+__all__ = [
+    "DitAttnError", "attention", "quantize_e4m3", "dit_attn_fwd", "dit_attn_fwd_ex", "dit_attn_quantize_e4m3",
+    "dit_attn_strerror", "dit_attn_version", "DIT_ATTN_BF16", "DIT_ATTN_FP8_E4M3", "DIT_ATTN_OK",
+    "DIT_ATTN_EINVAL", "DIT_ATTN_EUNSUPPORTED", "DIT_ATTN_EDEVICE", "DIT_ATTN_ELAUNCH",
+]
+
+
+class DitAttnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {dit_attn_strerror(status)} (status {status})")
+
+
+def _stream_handle(stream):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def attention(q, k, v, scale: float | None = None, *, out=None, lse=None, descale=None, stream=None):
+    """Dense non-causal attention of (B, H, N, d) device tensors.
+
+    bf16 inputs (d in {64, 128}) or float8_e4m3fn inputs (d = 128, with an
+    optional device float32 ``descale`` tensor [dq, dk, dv]). Returns the bf16
+    output; writes the natural-log row normaliser into ``lse`` (float32
+    (B, H, N)) when given. Runs on ``stream`` (default: torch's current
+    stream) without synchronising."""
+    import torch
+    if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v must share one (B, H, N, d) shape")
+    if q.dtype != k.dtype or q.dtype != v.dtype:
+        raise ValueError("q, k, v must share one dtype")
+    if q.dtype == torch.bfloat16:
+        dtype = DIT_ATTN_BF16
+    elif q.dtype == torch.float8_e4m3fn:
+        dtype = DIT_ATTN_FP8_E4M3
+    else:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    for t in (q, k, v):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("q, k, v must be contiguous device tensors")
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=q.device)
+    elif out.shape != q.shape or out.dtype != torch.bfloat16 or not out.is_contiguous():
+        raise ValueError("out must be a contiguous bf16 tensor of q's shape")
+    if lse is not None and (lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous()):
+        raise ValueError("lse must be a contiguous float32 (B, H, N) tensor")
+    if descale is not None and (descale.numel() != 3 or descale.dtype != torch.float32 or not descale.is_cuda):
+        raise ValueError("descale must be a float32 device tensor of 3 elements")
+    st = dit_attn_fwd_ex(q, k, v, out, B, H, N, d, float(scale), dtype, descale, lse, _stream_handle(stream))
+    if st != DIT_ATTN_OK:
+        raise DitAttnError(st, "dit_attn_fwd_ex")
+    return out
+
+
+def quantize_e4m3(x, *, out=None, descale=None, workspace=None, stream=None):
+    """Per-tensor absmax quantisation of a bf16 device tensor to float8_e4m3fn.
+
+    Returns (codes, descale) with ``descale`` a 1-element float32 device
+    tensor holding 1/s. ``workspace`` is a 1-element int32 device tensor."""
+    import torch
+    if x.dtype != torch.bfloat16 or not x.is_cuda or not x.is_contiguous():
+        raise ValueError("x must be a contiguous bf16 device tensor")
+    n = x.numel()
+    if out is None:
+        out = torch.empty(x.shape, dtype=torch.float8_e4m3fn, device=x.device)
+    if descale is None:
+        descale = torch.empty(1, dtype=torch.float32, device=x.device)
+    if workspace is None:
+        workspace = torch.empty(1, dtype=torch.int32, device=x.device)
+    st = dit_attn_quantize_e4m3(x, n, out, descale, workspace, _stream_handle(stream))
+    if st != DIT_ATTN_OK:
+        raise DitAttnError(st, "dit_attn_quantize_e4m3")
+    return out, descale

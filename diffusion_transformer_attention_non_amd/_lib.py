@@ -1,0 +1,70 @@
+"""ctypes binding of libditattn.so: the C entry points under the same names.
+
+Argument marshalling only. Every step of the attention runs in the HIP
+kernels behind the C ABI; nothing here computes. If the shared library is
+missing the import of this module fails loudly: there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libditattn.so")
+
+DIT_ATTN_BF16 = 0
+DIT_ATTN_FP8_E4M3 = 1
+DIT_ATTN_OK = 0
+DIT_ATTN_EINVAL = -1
+DIT_ATTN_EUNSUPPORTED = -2
+DIT_ATTN_EDEVICE = -3
+DIT_ATTN_ELAUNCH = -4
+
+EXPORTED = ("dit_attn_fwd", "dit_attn_fwd_ex", "dit_attn_quantize_e4m3", "dit_attn_strerror",
+            "dit_attn_version")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is not built; run `python -m diffusion_transformer_attention_non_amd.build` "
+                      "(or __graft_entry__.build()) first")
+
+_lib = ctypes.CDLL(LIB_PATH)
+_vp, _i, _f, _i64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_int64
+_lib.dit_attn_fwd.argtypes = [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _vp]
+_lib.dit_attn_fwd.restype = _i
+_lib.dit_attn_fwd_ex.argtypes = [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _vp, _vp, _vp]
+_lib.dit_attn_fwd_ex.restype = _i
+_lib.dit_attn_quantize_e4m3.argtypes = [_vp, _i64, _vp, _vp, _vp, _vp]
+_lib.dit_attn_quantize_e4m3.restype = _i
+_lib.dit_attn_strerror.argtypes = [_i]
+_lib.dit_attn_strerror.restype = ctypes.c_char_p
+_lib.dit_attn_version.argtypes = []
+_lib.dit_attn_version.restype = _i
+
+
+def _ptr(x):
+    """Raw device address of a tensor (or an int / None passed through)."""
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def dit_attn_fwd(q, k, v, o, B, H, N, d, scale, dtype, stream=None) -> int:
+    return _lib.dit_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, H, N, d, scale, dtype, _ptr(stream))
+
+
+def dit_attn_fwd_ex(q, k, v, o, B, H, N, d, scale, dtype, descale_qkv=None, lse=None, stream=None) -> int:
+    return _lib.dit_attn_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, H, N, d, scale, dtype,
+                                _ptr(descale_qkv), _ptr(lse), _ptr(stream))
+
+
+def dit_attn_quantize_e4m3(x, n, x8, descale, amax_ws, stream=None) -> int:
+    return _lib.dit_attn_quantize_e4m3(_ptr(x), n, _ptr(x8), _ptr(descale), _ptr(amax_ws), _ptr(stream))
+
+
+def dit_attn_strerror(status: int) -> str:
+    return _lib.dit_attn_strerror(status).decode()
+
+
+def dit_attn_version() -> int:
+    return _lib.dit_attn_version()

@@ -1,0 +1,174 @@
+// C ABI of the gfx950 DiT attention library: argument checks, device check,
+// kernel selection and launch on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "dit_attn.h"
+#include "attn_fwd_bf16.h"
+#include "attn_fwd_fp8.h"
+#include "quant_e4m3.h"
+
+using namespace ditattn;
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+// 0 = not checked yet, 1 = gfx950 and kernels configured, 2 = unsupported device
+std::atomic<int> g_device_state[kMaxDevices];
+
+// Kernel configurations. Rows per workgroup BR = NW * QB * 32.
+using CfgBf16D128 = Bf16Cfg<128, 1, 4, 64>;
+using CfgBf16D64 = Bf16Cfg<64, 2, 4, 64>;
+using CfgFp8D128 = Fp8Cfg<2, 4, 64>;
+
+template <class C>
+hipError_t allow_lds_bf16() {
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_fwd_bf16_kernel<C>),
+                             hipFuncAttributeMaxDynamicSharedMemorySize, C::kLdsBytes);
+}
+template <class C>
+hipError_t allow_lds_fp8() {
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_fwd_fp8_kernel<C>),
+                             hipFuncAttributeMaxDynamicSharedMemorySize, C::kLdsBytes);
+}
+
+int check_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return DIT_ATTN_EDEVICE;
+  int state = dev < kMaxDevices ? g_device_state[dev].load(std::memory_order_acquire) : 0;
+  if (state == 1) return DIT_ATTN_OK;
+  if (state == 2) return DIT_ATTN_EDEVICE;
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return DIT_ATTN_EDEVICE;
+  const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+  if (ok) {
+    if (allow_lds_bf16<CfgBf16D128>() != hipSuccess || allow_lds_bf16<CfgBf16D64>() != hipSuccess ||
+        allow_lds_fp8<CfgFp8D128>() != hipSuccess)
+      return DIT_ATTN_EDEVICE;
+  }
+  if (dev < kMaxDevices) g_device_state[dev].store(ok ? 1 : 2, std::memory_order_release);
+  return ok ? DIT_ATTN_OK : DIT_ATTN_EDEVICE;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+bool overlap(const void* a, uint64_t na, const void* b, uint64_t nb) {
+  const uintptr_t pa = reinterpret_cast<uintptr_t>(a), pb = reinterpret_cast<uintptr_t>(b);
+  return pa < pb + nb && pb < pa + na;
+}
+
+template <class C>
+int launch_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int BH, int N,
+                float scale, hipStream_t st) {
+  const int n_qtiles = (N + C::kBR - 1) / C::kBR;
+  const long long grid = (long long)n_qtiles * BH;
+  if (grid > 0x7fffffffLL) return DIT_ATTN_EINVAL;
+  const float scale_log2 = scale * 1.4426950408889634f;
+  hipLaunchKernelGGL(attn_fwd_bf16_kernel<C>, dim3((unsigned)grid), dim3(C::kThreads), C::kLdsBytes, st,
+                     static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                     static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), lse, N, n_qtiles,
+                     scale_log2, scale);
+  return hipGetLastError() == hipSuccess ? DIT_ATTN_OK : DIT_ATTN_ELAUNCH;
+}
+
+template <class C>
+int launch_fp8(const void* q, const void* k, const void* v, void* o, float* lse, const float* descale,
+               int BH, int N, float scale, hipStream_t st) {
+  const int n_qtiles = (N + C::kBR - 1) / C::kBR;
+  const long long grid = (long long)n_qtiles * BH;
+  if (grid > 0x7fffffffLL) return DIT_ATTN_EINVAL;
+  const float scale_log2 = scale * 1.4426950408889634f;
+  hipLaunchKernelGGL(attn_fwd_fp8_kernel<C>, dim3((unsigned)grid), dim3(C::kThreads), C::kLdsBytes, st,
+                     static_cast<const uint8_t*>(q), static_cast<const uint8_t*>(k),
+                     static_cast<const uint8_t*>(v), static_cast<uint16_t*>(o), lse, descale, N, n_qtiles,
+                     scale_log2, scale);
+  return hipGetLastError() == hipSuccess ? DIT_ATTN_OK : DIT_ATTN_ELAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+int dit_attn_version(void) { return (1 << 16) | 0; }
+
+const char* dit_attn_strerror(int status) {
+  switch (status) {
+    case DIT_ATTN_OK: return "ok";
+    case DIT_ATTN_EINVAL: return "invalid argument";
+    case DIT_ATTN_EUNSUPPORTED: return "unsupported head dimension or dtype";
+    case DIT_ATTN_EDEVICE: return "no gfx950 HIP device is current";
+    case DIT_ATTN_ELAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+int dit_attn_fwd_ex(const void* q, const void* k, const void* v, void* o, int B, int H, int N, int d,
+                    float scale, int dtype, const float* descale_qkv, float* lse, void* stream) {
+  if (!q || !k || !v || !o) return DIT_ATTN_EINVAL;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16)) return DIT_ATTN_EINVAL;
+  if (lse && !aligned(lse, 4)) return DIT_ATTN_EINVAL;
+  if (descale_qkv && !aligned(descale_qkv, 4)) return DIT_ATTN_EINVAL;
+  if (B < 1 || H < 1 || N < 1) return DIT_ATTN_EINVAL;
+  if (!std::isfinite(scale) || !(scale > 0.f)) return DIT_ATTN_EINVAL;
+  if (dtype != DIT_ATTN_BF16 && dtype != DIT_ATTN_FP8_E4M3) return DIT_ATTN_EUNSUPPORTED;
+  if (dtype == DIT_ATTN_BF16 && d != 64 && d != 128) return DIT_ATTN_EUNSUPPORTED;
+  if (dtype == DIT_ATTN_FP8_E4M3 && d != 128) return DIT_ATTN_EUNSUPPORTED;
+  // element count B*H*N*d < 2^62 without overflow (each factor < 2^31)
+  const unsigned __int128 elems = (unsigned __int128)B * (unsigned)H * (unsigned)N * (unsigned)d;
+  if (elems >= ((unsigned __int128)1 << 62)) return DIT_ATTN_EINVAL;
+  const long long bh = (long long)B * H;
+  if (bh > 0x7fffffffLL) return DIT_ATTN_EINVAL;
+  const uint64_t in_bytes = (uint64_t)elems * (dtype == DIT_ATTN_BF16 ? 2u : 1u);
+  const uint64_t out_bytes = (uint64_t)elems * 2u;
+  if (overlap(o, out_bytes, q, in_bytes) || overlap(o, out_bytes, k, in_bytes) ||
+      overlap(o, out_bytes, v, in_bytes))
+    return DIT_ATTN_EINVAL;
+  if (lse) {
+    const uint64_t lse_bytes = (uint64_t)bh * (uint64_t)N * 4u;
+    if (overlap(lse, lse_bytes, q, in_bytes) || overlap(lse, lse_bytes, k, in_bytes) ||
+        overlap(lse, lse_bytes, v, in_bytes) || overlap(lse, lse_bytes, o, out_bytes))
+      return DIT_ATTN_EINVAL;
+  }
+  const int dev_status = check_device();
+  if (dev_status != DIT_ATTN_OK) return dev_status;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (dtype == DIT_ATTN_BF16) {
+    if (d == 128) return launch_bf16<CfgBf16D128>(q, k, v, o, lse, (int)bh, N, scale, st);
+    return launch_bf16<CfgBf16D64>(q, k, v, o, lse, (int)bh, N, scale, st);
+  }
+  return launch_fp8<CfgFp8D128>(q, k, v, o, lse, descale_qkv, (int)bh, N, scale, st);
+}
+
+int dit_attn_fwd(const void* q, const void* k, const void* v, void* o, int B, int H, int N, int d, float scale,
+                 int dtype, void* stream) {
+  return dit_attn_fwd_ex(q, k, v, o, B, H, N, d, scale, dtype, nullptr, nullptr, stream);
+}
+
+int dit_attn_quantize_e4m3(const void* x, int64_t n, void* x8, float* descale, uint32_t* amax_ws,
+                           void* stream) {
+  if (!x || !x8 || !descale || !amax_ws) return DIT_ATTN_EINVAL;
+  if (!aligned(x, 16) || !aligned(x8, 16) || !aligned(descale, 4) || !aligned(amax_ws, 4)) return DIT_ATTN_EINVAL;
+  if (n < 1 || n % 8 != 0 || n >= ((int64_t)1 << 62)) return DIT_ATTN_EINVAL;
+  if (overlap(x, (uint64_t)n * 2u, x8, (uint64_t)n) || overlap(descale, 4, x, (uint64_t)n * 2u) ||
+      overlap(descale, 4, x8, (uint64_t)n) || overlap(amax_ws, 4, x, (uint64_t)n * 2u) ||
+      overlap(amax_ws, 4, x8, (uint64_t)n) || overlap(amax_ws, 4, descale, 4))
+    return DIT_ATTN_EINVAL;
+  const int dev_status = check_device();
+  if (dev_status != DIT_ATTN_OK) return dev_status;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int64_t n8 = n / 8;
+  const int64_t want = (n8 + kQuantThreads - 1) / kQuantThreads;
+  const unsigned blocks = (unsigned)(want < 2048 ? want : 2048);
+  const uint16_t* xb = static_cast<const uint16_t*>(x);
+  hipLaunchKernelGGL(amax_clear_kernel, dim3(1), dim3(64), 0, st, amax_ws);
+  hipLaunchKernelGGL(amax_kernel, dim3(blocks), dim3(kQuantThreads), 0, st, xb, n8, amax_ws);
+  hipLaunchKernelGGL(quant_e4m3_kernel, dim3(blocks), dim3(kQuantThreads), 0, st, xb, n8,
+                     static_cast<uint8_t*>(x8), descale, static_cast<const uint32_t*>(amax_ws));
+  return hipGetLastError() == hipSuccess ? DIT_ATTN_OK : DIT_ATTN_ELAUNCH;
+}
+
+}  // extern "C"

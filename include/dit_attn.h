@@ -1,0 +1,130 @@
+/*
+ * dit_attn.h - C ABI of the MI355X (gfx950) DiT joint-attention library.
+ *
+ * The operation is the dense, non-causal multi-head attention of a diffusion
+ * transformer over the concatenated text and image token sequence:
+ *
+ *     O[b,h] = softmax(Q[b,h] K[b,h]^T * scale) V[b,h]
+ *
+ * The pages this library follows name it only as the DiT's "dense" BF16
+ * attention, about 60% of DiT kernel time at 2048x2048 ("Speed Up Image
+ * Generation with FLUX 3 Image Klein on NVIDIA Blackwell GPUs", "Key
+ * takeaways"; Italian commentary, section "NVFP4, attention e caching"), and
+ * report FP8 attention variants beside it (Japanese summary, third paragraph).
+ * No mask is applied: every token attends to every token (the card's
+ * glossary entry "transformer").
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Layout:    q, k, v, o are contiguous row-major [B][H][N][d] tensors, d
+ *            innermost, in device memory. o is always bfloat16.
+ * Ownership: the caller allocates, owns and frees every buffer. The library
+ *            never allocates, frees or retains memory, never synchronises,
+ *            and keeps no state beyond its loaded code objects and a
+ *            per-device "is gfx950" flag.
+ * Streams:   work is enqueued on `stream` (a hipStream_t; NULL = the null
+ *            stream) and the call returns at once. The calls contain no host
+ *            synchronisation, allocation or device-to-host read, so they may
+ *            be captured in a HIP graph.
+ * Errors:    every entry point returns DIT_ATTN_OK or a negative status, and
+ *            launches nothing when it returns an error other than
+ *            DIT_ATTN_ELAUNCH. Faults inside a kernel are not seen by the
+ *            call; the caller sees them when it synchronises the stream.
+ * Threads:   re-entrant; any number of host threads may call on their own
+ *            streams.
+ */
+#ifndef DIT_ATTN_H
+#define DIT_ATTN_H
+
+#include <stdint.h>
+
+#if defined(__GNUC__) || defined(__clang__)
+#define DIT_ATTN_API __attribute__((visibility("default")))
+#else
+#define DIT_ATTN_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    DIT_ATTN_BF16 = 0,      /* q, k, v bfloat16 */
+    DIT_ATTN_FP8_E4M3 = 1   /* q, k, v OCP FP8 E4M3FN bytes with per-tensor descales */
+} dit_attn_dtype_t;
+
+enum {
+    DIT_ATTN_OK = 0,
+    DIT_ATTN_EINVAL = -1,        /* NULL / misaligned / aliasing pointer, B, H or N < 1, bad scale, size overflow */
+    DIT_ATTN_EUNSUPPORTED = -2,  /* head dimension or dtype not implemented */
+    DIT_ATTN_EDEVICE = -3,       /* no HIP device, or the current device is not gfx950 */
+    DIT_ATTN_ELAUNCH = -4        /* the kernel launch itself failed */
+};
+
+/*
+ * dit_attn_fwd - attention forward.
+ *
+ * q, k, v : device pointers, [B][H][N][d], bfloat16 (dtype = DIT_ATTN_BF16)
+ *           or e4m3 bytes (dtype = DIT_ATTN_FP8_E4M3, descales taken as 1).
+ *           16-byte aligned.
+ * o       : device pointer, [B][H][N][d] bfloat16, 16-byte aligned, must not
+ *           overlap q, k or v.
+ * B, H, N : batch entries, heads, tokens (text + image [+ reference image]);
+ *           each >= 1, and B*H*N*d < 2^62.
+ * d       : head dimension. bf16: 64 or 128. fp8: 128.
+ * scale   : logit multiplier (1/sqrt(d) for standard attention); finite, > 0.
+ * dtype   : a dit_attn_dtype_t value.
+ * stream  : hipStream_t or NULL.
+ *
+ * Status: DIT_ATTN_EINVAL, _EUNSUPPORTED or _EDEVICE before any launch;
+ * DIT_ATTN_ELAUNCH if hipLaunchKernel reports an error.
+ */
+DIT_ATTN_API int dit_attn_fwd(const void* q, const void* k, const void* v, void* o,
+                 int B, int H, int N, int d, float scale, int dtype, void* stream);
+
+/*
+ * dit_attn_fwd_ex - dit_attn_fwd plus the inputs the short form cannot carry.
+ *
+ * descale_qkv : device float[3] {dq, dk, dv}: the fp8 dequantisation factors
+ *               (real value = code value * descale). NULL means 1, 1, 1.
+ *               Ignored for bf16. The logits use scale*dq*dk and O carries dv.
+ * lse         : device float[B*H*N] or NULL. When given, row i of head (b,h)
+ *               receives the natural-log normaliser
+ *               log(sum_j exp(s_ij)), s_ij the scaled logits, at [b*H*N + h*N + i].
+ *               Must not overlap any other buffer. 4-byte aligned.
+ */
+DIT_ATTN_API int dit_attn_fwd_ex(const void* q, const void* k, const void* v, void* o,
+                    int B, int H, int N, int d, float scale, int dtype,
+                    const float* descale_qkv, float* lse, void* stream);
+
+/*
+ * dit_attn_quantize_e4m3 - per-tensor absmax quantisation of a bf16 tensor.
+ *
+ * Produces the fp8 inputs of the DIT_ATTN_FP8_E4M3 path on the device:
+ *   amax = max |x|;  s = fp32(448 / amax)  (s = 1 if amax is 0 or s is not finite)
+ *   x8[i] = e4m3 round-to-nearest-even of clamp(fp32(x[i] * s), -448, 448)
+ *   *descale = fp32(1 / s)
+ *
+ * x        : device bfloat16[n], 16-byte aligned.
+ * n        : element count, 1 <= n < 2^62, a multiple of 8.
+ * x8       : device uint8[n], 16-byte aligned, not overlapping x.
+ * descale  : device float[1]: receives 1/s.
+ * amax_ws  : device uint32[1] workspace owned by the caller; the call clears
+ *            it itself (with a kernel), then reduces into it. Two calls in
+ *            flight at once must not share it.
+ * stream   : hipStream_t or NULL.
+ */
+DIT_ATTN_API int dit_attn_quantize_e4m3(const void* x, int64_t n, void* x8, float* descale,
+                           uint32_t* amax_ws, void* stream);
+
+/* Human-readable name of a status code (static string, never NULL). */
+DIT_ATTN_API const char* dit_attn_strerror(int status);
+
+/* Library ABI version: (major << 16) | minor. */
+DIT_ATTN_API int dit_attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DIT_ATTN_H */

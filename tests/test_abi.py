@@ -1,0 +1,93 @@
+"""The C-ABI library loads, exports what include/dit_attn.h declares, and rejects
+bad arguments on the host before any launch. No compute call is made here."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dit_attn.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"DIT_ATTN_API\s+[\w\s\*]+?\b(dit_attn_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import diffusion_transformer_attention_non_amd as pkg
+    return pkg
+
+
+def test_header_declares_the_entry_points():
+    assert _declared() == sorted(["dit_attn_fwd", "dit_attn_fwd_ex", "dit_attn_quantize_e4m3",
+                                  "dit_attn_strerror", "dit_attn_version"])
+
+
+def test_library_exports_every_declared_symbol(lib):
+    so = ctypes.CDLL(lib._lib.LIB_PATH)
+    for name in _declared():
+        assert hasattr(so, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", lib._lib.LIB_PATH], capture_output=True, text=True).stdout
+    exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
+    assert set(_declared()) <= exported
+    assert set(lib._lib.EXPORTED) == set(_declared())
+
+
+def test_strerror_and_version(lib):
+    assert lib.dit_attn_version() >> 16 == 1
+    for st in (0, -1, -2, -3, -4, 7):
+        assert isinstance(lib.dit_attn_strerror(st), str) and lib.dit_attn_strerror(st)
+    assert lib.dit_attn_strerror(-2) != lib.dit_attn_strerror(-1)
+
+
+A, B_, C, O = 0x10000, 0x20000, 0x30000, 0x40000   # fake, aligned, disjoint addresses (never dereferenced)
+
+
+@pytest.mark.parametrize("args,expect", [
+    ((0, B_, C, O, 1, 1, 8, 64, 0.125, 0), -1),           # NULL q
+    ((A, B_, C, 0, 1, 1, 8, 64, 0.125, 0), -1),           # NULL o
+    ((A + 2, B_, C, O, 1, 1, 8, 64, 0.125, 0), -1),       # misaligned q
+    ((A, B_, C, O + 8, 1, 1, 8, 64, 0.125, 0), -1),       # misaligned o
+    ((A, B_, C, O, 0, 1, 8, 64, 0.125, 0), -1),           # B < 1
+    ((A, B_, C, O, 1, 0, 8, 64, 0.125, 0), -1),           # H < 1
+    ((A, B_, C, O, 1, 1, 0, 64, 0.125, 0), -1),           # N < 1
+    ((A, B_, C, O, 1, 1, 8, 64, 0.0, 0), -1),             # scale 0
+    ((A, B_, C, O, 1, 1, 8, 64, -1.0, 0), -1),            # negative scale
+    ((A, B_, C, O, 1, 1, 8, 64, float("nan"), 0), -1),    # NaN scale
+    ((A, B_, C, O, 1, 1, 8, 64, float("inf"), 0), -1),    # inf scale
+    ((A, B_, C, O, 1, 1, 8, 96, 0.125, 0), -2),           # d = 96 not implemented
+    ((A, B_, C, O, 1, 1, 8, 64, 0.125, 1), -2),           # fp8 needs d = 128
+    ((A, B_, C, O, 1, 1, 8, 64, 0.125, 5), -2),           # unknown dtype
+    ((A, B_, C, A, 1, 1, 8, 64, 0.125, 0), -1),           # o aliases q
+    ((A, B_, C, C + 256, 1, 1, 8, 64, 0.125, 0), -1),     # o overlaps v (v spans 1 KiB)
+    ((A, B_, C, O, 2**30, 2**30, 2**30, 128, 0.125, 0), -1),  # size overflow
+])
+def test_fwd_rejects_bad_arguments_before_launch(lib, args, expect):
+    assert lib.dit_attn_fwd(*args, None) == expect
+    assert lib.dit_attn_fwd_ex(*args, None, None, None) == expect
+
+
+def test_fwd_ex_rejects_bad_lse(lib):
+    args = (A, B_, C, O, 1, 1, 8, 64, 0.125, 0)
+    assert lib.dit_attn_fwd_ex(*args, None, 0x50002, None) == -1      # misaligned lse
+    assert lib.dit_attn_fwd_ex(*args, None, O + 4, None) == -1        # lse overlaps o
+    assert lib.dit_attn_fwd_ex(*args, 0x50002, None, None) == -1      # misaligned descale
+
+
+def test_quantize_rejects_bad_arguments(lib):
+    assert lib.dit_attn_quantize_e4m3(0, 64, B_, C, O, None) == -1
+    assert lib.dit_attn_quantize_e4m3(A, 60, B_, C, O, None) == -1    # n not a multiple of 8
+    assert lib.dit_attn_quantize_e4m3(A, 0, B_, C, O, None) == -1
+    assert lib.dit_attn_quantize_e4m3(A, 64, A + 64, C, O, None) == -1  # x8 overlaps x
+    assert lib.dit_attn_quantize_e4m3(A, 64, B_, O, O, None) == -1      # descale aliases ws
+
+
+def test_valid_call_without_gpu_reports_device_error(lib):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present; covered by the GPU tests")
+    assert lib.dit_attn_fwd(A, B_, C, O, 1, 1, 8, 64, 0.125, 0, None) == -3

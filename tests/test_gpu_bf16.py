@@ -1,0 +1,143 @@
+"""GPU parity of the bf16 path against the fp64 oracle, through the C ABI."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from parity import check_bf16, gpu_attention, say
+from workloads import (WORKLOADS, coverage_pattern, constant_values, dominating_key, identical_keys,
+                       make_qkv, random_qkv, sample_rows)
+
+pytestmark = pytest.mark.gpu
+
+
+def _full_check(q, k, v, scale, label, lse=True):
+    say(f"[gpu] {label}: shape {tuple(q.shape)}")
+    o, l = gpu_attention(q, k, v, scale, want_lse=lse)
+    o_ref, l_ref, a_ref = oracle.attention(q, k, v, scale, want_abs=True)
+    check_bf16(o, o_ref, a_ref, label)
+    if lse:
+        assert np.allclose(l, l_ref, rtol=2e-6, atol=2e-5), float(np.abs(l - l_ref).max())
+    return o
+
+
+def test_tiny_workload_full():
+    w = WORKLOADS["tiny"]
+    q, k, v = make_qkv(w)
+    _full_check(q, k, v, 1 / math.sqrt(w.d), "tiny B=1 H=2 N=256 d=64")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("N", [1, 2, 31, 63, 64, 65, 127, 129, 300, 1000])
+def test_odd_lengths(N, d):
+    q, k, v = random_qkv(1, 2, N, d, seed=N + d)
+    _full_check(q, k, v, 1 / math.sqrt(d), f"N={N} d={d}")
+
+
+def test_batch_heads_and_peaked_small():
+    q, k, v = random_qkv(2, 3, 777, 128, seed=5)
+    _full_check(q * 4, k, v, 1 / math.sqrt(128), "B=2 H=3 N=777 peaked")
+
+
+@pytest.mark.parametrize("name,stride", [("t2i_1024", 16), ("t2i_2048", 64), ("t2i_2048_peaked", 64),
+                                         ("i2i_2048", 96)])
+def test_workload_sampled_rows(name, stride):
+    w = WORKLOADS[name]
+    q, k, v = make_qkv(w)
+    scale = 1 / math.sqrt(w.d)
+    say(f"[gpu] {name}: B={w.B} H={w.H} N={w.N} d={w.d}")
+    o, l = gpu_attention(q, k, v, scale, want_lse=True)
+    rows = sample_rows(w.N, seed=0, n_edge=128, stride=stride)
+    o_ref, l_ref, a_ref = oracle.attention(q, k, v, scale, rows=rows, want_abs=True)
+    check_bf16(o[:, :, rows], o_ref, a_ref, f"{name} ({rows.size} rows/head)")
+    assert np.allclose(l[:, :, rows], l_ref, rtol=2e-6, atol=2e-5)
+
+
+# ------------------------------------------------------------ exact structure
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("N", [300, 4608, 16896])
+def test_tile_coverage_exact(N, d):
+    """All logits equal and V one-hot by 64-key block: O[c] = (#tokens j with
+    (j // 64) % d == c) / N, exact in fp32 then one bf16 rounding. A dropped or
+    repeated key block moves some channel by 64/N."""
+    q, k, v = coverage_pattern(1, 2, N, d, block=64)
+    say(f"[gpu] coverage N={N} d={d}")
+    o, _ = gpu_attention(q, k, v, 1 / math.sqrt(d))
+    j = np.arange(N)
+    counts = np.bincount((j // 64) % d, minlength=d).astype(np.float64)
+    exact = np.broadcast_to(counts / N, o.shape)
+    # one bf16 rounding (half an ulp) plus fp32 noise; a dropped block moves a channel by ~50%
+    assert (np.abs(o - exact) <= 2.0**-8 * exact).all(), np.abs(o - exact).max()
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_dominating_key_every_position(d):
+    N = 300
+    for j_star in range(N):
+        q, k, v = dominating_key(1, 1, N, d, j_star, seed=j_star)
+        o, _ = gpu_attention(q, k, v, 1 / math.sqrt(d))
+        ref = v[:, :, j_star:j_star + 1].double().numpy()
+        assert np.array_equal(o, np.broadcast_to(ref, o.shape)), j_star
+
+
+def test_dominating_key_tile_edges_long():
+    N, d = 16896, 128
+    for j_star in [0, 1, 31, 32, 63, 64, 127, 128, 8191, 8192, N - 65, N - 64, N - 1]:
+        say(f"[gpu] dominating key N={N} j*={j_star}")
+        q, k, v = dominating_key(1, 1, N, d, j_star, seed=j_star)
+        o, _ = gpu_attention(q, k, v, 1 / math.sqrt(d))
+        ref = v[:, :, j_star:j_star + 1].double().numpy()
+        assert np.array_equal(o, np.broadcast_to(ref, o.shape)), j_star
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_constant_values_and_identical_keys(d):
+    q, k, v = constant_values(1, 2, 1000, d, seed=1, c=0.75)
+    o, _ = gpu_attention(q, k, v, 1 / math.sqrt(d))
+    # rows of p sum to one: only the bf16 rounding of p (<= 2^-8 relative) separates O from c
+    assert np.abs(o - 0.75).max() <= 2.0**-8 * 0.75
+    q, k, v = identical_keys(1, 2, 1000, d, seed=2)
+    o, _ = gpu_attention(q, k, v, 1 / math.sqrt(d))
+    mean = oracle.bf16_round(v.double().numpy().mean(axis=2, keepdims=True))
+    assert np.abs(o - mean).max() <= 2.0**-8 * np.abs(mean).max() + 1e-6
+
+
+def test_single_token_is_exact():
+    q, k, v = random_qkv(2, 3, 1, 128, seed=9)
+    o, _ = gpu_attention(q, k, v, 0.1)
+    assert np.array_equal(o, v.double().numpy())
+
+
+def test_joint_key_value_permutation_and_query_permutation():
+    q, k, v = random_qkv(1, 2, 2000, 128, seed=11)
+    scale = 1 / math.sqrt(128)
+    g = torch.Generator().manual_seed(3)
+    pk = torch.randperm(2000, generator=g)
+    pq = torch.randperm(2000, generator=g)
+    o, _ = gpu_attention(q, k, v, scale)
+    o_k, _ = gpu_attention(q, k[:, :, pk].contiguous(), v[:, :, pk].contiguous(), scale)
+    o_q, _ = gpu_attention(q[:, :, pq].contiguous(), k, v, scale)
+    o_ref, _, a_ref = oracle.attention(q, k, v, scale, want_abs=True)
+    check_bf16(o_k, o_ref, a_ref, "K/V permuted")
+    check_bf16(o_q, o_ref[:, :, pq.numpy()], a_ref[:, :, pq.numpy()], "Q permuted")
+    assert np.abs(o_k - o).max() <= 2 * (2.0**-8) * (np.abs(o_ref).max() + a_ref.max())
+
+
+def test_deterministic_and_heads_independent():
+    q, k, v = random_qkv(2, 3, 1500, 128, seed=12)
+    scale = 1 / math.sqrt(128)
+    o1, l1 = gpu_attention(q, k, v, scale, want_lse=True)
+    o2, l2 = gpu_attention(q, k, v, scale, want_lse=True)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+    o_one, _ = gpu_attention(q[1:2, 2:3].contiguous(), k[1:2, 2:3].contiguous(), v[1:2, 2:3].contiguous(), scale)
+    assert np.array_equal(o_one[0, 0], o1[1, 2])
+
+
+def test_unsupported_head_dim_on_device():
+    import diffusion_transformer_attention_non_amd as dit
+    x = torch.zeros((1, 1, 64, 96), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(dit.DitAttnError) as e:
+        dit.attention(x, x, x)
+    assert e.value.status == dit.DIT_ATTN_EUNSUPPORTED

@@ -1,0 +1,127 @@
+"""GPU parity of the fp8-e4m3 path: the on-device quantiser bit for bit against
+the oracle's quantiser, and the fp8 attention against the fp64 oracle.
+
+Gates for the fp8 attention (bf16 output):
+* spec: max |O_gpu - O| <= 6e-2 against the exact oracle on the unquantised
+  bf16 inputs, at the 16896-token workload it is stated for.
+* calibrated: the fp64 emulation of the fp8 pipeline (same e4m3 inputs, P
+  rounded to e4m3 after scaling by 2^8) has error e_emul against the same
+  exact oracle. The kernel rounds P relative to its running maximum rather
+  than the final row maximum, so its P rounding noise is statistically alike
+  but not identical; the input quantisation, which dominates, is bit-identical.
+  Gate: mean error <= 1.25 e_emul(mean) + 1e-5 and max error <= 2 e_emul(max).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from parity import SPEC_MAX_FP8, gpu_attention, say
+from workloads import WORKLOADS, coverage_pattern, make_qkv, random_qkv, sample_rows
+
+pytestmark = pytest.mark.gpu
+
+
+def _gpu_quantize(x):
+    import diffusion_transformer_attention_non_amd as dit
+    codes, descale = dit.quantize_e4m3(x.to("cuda"))
+    torch.cuda.synchronize()
+    return codes, descale
+
+
+def _check_quantizer(x, label):
+    codes, descale = _gpu_quantize(x)
+    ref_codes, ref_descale, _ = oracle.quantize_per_tensor(x)
+    got = codes.view(torch.uint8).cpu().numpy().reshape(-1)
+    assert descale.item() == float(ref_descale), (label, descale.item(), ref_descale)
+    ref = ref_codes.reshape(-1)
+    assert np.array_equal(got, ref), (label, int((got != ref).sum()))
+    return codes, descale
+
+
+def test_quantizer_bit_exact_small_and_edge_values():
+    g = torch.Generator().manual_seed(0)
+    for n, std in [(8, 1.0), (64, 1e-3), (4096, 30.0), (100000, 1.0)]:
+        x = (torch.randn(n, generator=g) * std).to(torch.bfloat16)
+        _check_quantizer(x, f"n={n} std={std}")
+    x = torch.zeros(64, dtype=torch.bfloat16)
+    codes, descale = _gpu_quantize(x)
+    assert descale.item() == 1.0 and not codes.view(torch.uint8).any()
+    # values straddling e4m3 rounding ties after scaling
+    vals = oracle.e4m3_decode(np.arange(0, 0x7E, dtype=np.uint8))
+    mids = np.concatenate([vals, (vals[:-1] + vals[1:]) / 2, [448.0]])
+    x = torch.from_numpy(np.concatenate([mids, -mids, np.zeros(8 - (2 * mids.size) % 8)])).to(torch.bfloat16)
+    _check_quantizer(x, "ties")
+
+
+def test_quantizer_bit_exact_full_workload():
+    w = WORKLOADS["t2i_2048_fp8"]
+    for t, name in zip(make_qkv(w), "qkv"):
+        say(f"[gpu] quantise {name} {tuple(t.shape)}")
+        _check_quantizer(t.reshape(-1), f"{name} full")
+
+
+def _fp8_inputs_gpu(q, k, v):
+    qs = [_gpu_quantize(t.reshape(-1)) for t in (q, k, v)]
+    codes = [c.view(q.shape) for c, _ in qs]
+    descale = torch.cat([d for _, d in qs]).contiguous()
+    return codes, descale
+
+
+def _run_fp8(q, k, v, scale):
+    import diffusion_transformer_attention_non_amd as dit
+    (q8, k8, v8), descale = _fp8_inputs_gpu(q, k, v)
+    B, H, N, d = q.shape
+    lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+    o = dit.attention(q8, k8, v8, scale, descale=descale, lse=lse)
+    torch.cuda.synchronize()
+    return o.float().cpu().double().numpy(), lse.cpu().double().numpy()
+
+
+def _check_fp8(q, k, v, scale, label, rows=None, spec_gate=False):
+    say(f"[gpu] fp8 {label}: shape {tuple(q.shape)}")
+    o, lse = _run_fp8(q, k, v, scale)
+    if rows is None:
+        rows = np.arange(q.shape[2])
+    o = o[:, :, rows]
+    o_ref, _ = oracle.attention(q, k, v, scale, rows=rows)
+    (q8, dq, _), (k8, dk, _), (v8, dv, _) = (oracle.quantize_per_tensor(t) for t in (q, k, v))
+    o_emul, lse_emul = oracle.attention_fp8_pipeline(q8, k8, v8, dq, dk, dv, scale, rows=rows)
+    err = np.abs(o - o_ref)
+    err_e = np.abs(o_emul - o_ref)
+    say(f"  {label}: gpu max {err.max():.3e} mean {err.mean():.3e} | emulation max {err_e.max():.3e} "
+        f"mean {err_e.mean():.3e}")
+    assert np.isfinite(o).all()
+    if spec_gate:
+        # the 6e-2 figure is stated for the 16896-token shape; at small N (N = 1: O is the
+        # quantised V itself) the e4m3 input rounding alone exceeds it for any correct pipeline
+        assert err.max() <= SPEC_MAX_FP8
+    assert err.mean() <= 1.25 * err_e.mean() + 1e-5
+    assert err.max() <= 2.0 * err_e.max() + 1e-5
+    assert np.allclose(lse[:, :, rows], lse_emul, rtol=1e-5, atol=1e-4)
+
+
+@pytest.mark.parametrize("N", [1, 65, 300, 1000])
+def test_fp8_small(N):
+    q, k, v = random_qkv(1, 2, N, 128, seed=100 + N)
+    _check_fp8(q, k, v, 1 / math.sqrt(128), f"N={N}")
+
+
+def test_fp8_workload_sampled_rows():
+    w = WORKLOADS["t2i_2048_fp8"]
+    q, k, v = make_qkv(w)
+    rows = sample_rows(w.N, seed=0, n_edge=128, stride=64)
+    _check_fp8(q, k, v, 1 / math.sqrt(128), "t2i_2048_fp8", rows=rows, spec_gate=True)
+
+
+def test_fp8_tile_coverage_exact():
+    """Equal logits and one-hot V (exact in e4m3 after scaling by 448): every
+    probability is 1, so O[c] = count_c / N up to the bf16 output rounding."""
+    N = 16896
+    q, k, v = coverage_pattern(1, 2, N, 128, block=64)
+    o, _ = _run_fp8(q, k, v, 1 / math.sqrt(128))
+    j = np.arange(N)
+    exact = np.broadcast_to(np.bincount((j // 64) % 128, minlength=128) / N, o.shape)
+    assert (np.abs(o - exact) <= 2.0**-8 * exact).all(), np.abs(o - exact).max()
