@@ -113,6 +113,9 @@ def main(argv=None):
     ap.add_argument("--no-fp8", action="store_true", help="skip the fp8-e4m3 companion measurement")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB three times (to calibrate "
+                         "the FETCH_SIZE / WRITE_SIZE counters against known bytes) and exit")
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -122,6 +125,15 @@ def main(argv=None):
         return 2
 
     import torch
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_per_copy": n, "copies": 3}), flush=True)
+        return 0
     import diffusion_transformer_attention_non_amd as dit
     from workloads import WORKLOADS, make_qkv
 

@@ -23,9 +23,9 @@
 
 namespace ditattn {
 
-template <int D, int QB, int NW, int KB>
+template <int D, int QB, int NW, int KB, int VSWZ = 2>
 struct Bf16Cfg {
-  static constexpr int kD = D, kQB = QB, kNW = NW, kKB = KB;
+  static constexpr int kD = D, kQB = QB, kNW = NW, kKB = KB, kVSwz = VSWZ;
   static constexpr int kThreads = NW * 64;
   static constexpr int kBR = NW * QB * 32;          // query rows per workgroup
   static constexpr int kKS = D / 16;                // MFMA k-steps over d
@@ -45,6 +45,30 @@ struct Bf16Cfg {
 template <int CHUNKS>
 __device__ __forceinline__ int swz(int r, int c) {
   return r * (CHUNKS * 16) + ((c ^ (r & (CHUNKS - 1))) << 4);
+}
+
+// V tiles are read with ds_read_b64_tr_b16: each 16-lane group reads 4
+// consecutive rows x 32 contiguous bytes (one 32-byte pair of chunks), and the
+// two groups of a half-wave read neighbouring pairs of the same rows.
+// Swizzling 16-byte chunks by row (MODE 0) leaves rows r and r^1 on the same
+// 32-byte bank slots. MODE 1 XORs the pair index with (row mod 8): the 4 rows
+// of one group land on 4 distinct 32-byte slots of 128 bytes. MODE 2 XORs it
+// with f(row mod 4), f = {0, 3, 5, 6}: distinct in the low two bits (4 rows
+// of one group over 128 bytes) and, together with their neighbour pair
+// (f ^ 1), 8 distinct slots over 256 bytes (both groups of a half-wave).
+// Stores of whole rows stay conflict-free since a row's pairs are permuted.
+template <int CHUNKS, int MODE = 2>
+__device__ __forceinline__ int swz_v(int r, int c) {
+  if constexpr (MODE == 0) {
+    return r * (CHUNKS * 16) + ((c ^ (r & (CHUNKS - 1))) << 4);
+  } else if constexpr (MODE == 1) {
+    constexpr int kPairMask = (CHUNKS / 2 < 8 ? CHUNKS / 2 : 8) - 1;
+    return r * (CHUNKS * 16) + ((((c >> 1) ^ (r & kPairMask)) << 5) | ((c & 1) << 4));
+  } else {
+    constexpr int kPairMask = CHUNKS / 2 - 1;
+    const int f = (0x6530 >> ((r & 3) * 4)) & 7;      // f(0..3) = 0, 3, 5, 6
+    return r * (CHUNKS * 16) + (((((c >> 1) ^ f) & kPairMask) << 5) | ((c & 1) << 4));
+  }
 }
 
 constexpr float kTauBf16 = 8.0f;
@@ -123,7 +147,7 @@ void attn_fwd_bf16_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __res
       const int ci = tid + i * C::kThreads;
       const int r = ci / CH, c = ci % CH;
       *(i32x4_t*)(kb + swz<CH>(r, c)) = stK[i];
-      *(i32x4_t*)(vb + swz<CH>(r, c)) = stV[i];
+      *(i32x4_t*)(vb + swz_v<CH, C::kVSwz>(r, c)) = stV[i];
     }
   };
 
@@ -236,9 +260,9 @@ void attn_fwd_bf16_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __res
         for (int db = 0; db < DB; ++db) {
           const int c = db * 4 + tr_chunk;
           const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              DIT_LDS(i16x4_t, vbuf + swz<CH>(rbase, c) + tr_off));
+              DIT_LDS(i16x4_t, (vbuf + swz_v<CH, C::kVSwz>(rbase, c) + tr_off)));
           const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              DIT_LDS(i16x4_t, vbuf + swz<CH>(rbase + 8, c) + tr_off));
+              DIT_LDS(i16x4_t, (vbuf + swz_v<CH, C::kVSwz>(rbase + 8, c) + tr_off)));
           const i32x2_t lo2 = __builtin_bit_cast(i32x2_t, lo), hi2 = __builtin_bit_cast(i32x2_t, hi);
           const i32x4_t a4 = {lo2[0], lo2[1], hi2[0], hi2[1]};
           const bf16x8_t a = __builtin_bit_cast(bf16x8_t, a4);

@@ -39,9 +39,20 @@ struct Fp8Cfg {
 constexpr float kTauFp8 = 4.0f;
 constexpr float kPScaleFp8 = 16.0f;     // 2^(8 - TAU)
 
-template <int CHUNKS>
-__device__ __forceinline__ int swz8(int r, int c) {
-  return r * (CHUNKS * 16) + ((c ^ (r & (CHUNKS - 1))) << 4);
+// LDS serves 256 bytes (64 four-byte banks) per pass; with 128-byte rows two
+// rows share a pass, one in each half (row parity). Both swizzles below
+// permute the 16-byte chunks inside a row, so row-wise stores stay
+// conflict-free.
+// K tiles: a ds_read_b128 pass covers rows 0..15 of one chunk column. The
+// rows of each parity need 8 distinct chunks: XOR with (row >> 1) mod 8.
+__device__ __forceinline__ int swz8_k(int r, int c) {
+  return r * 128 + ((c ^ ((r >> 1) & 7)) << 4);
+}
+// V tiles: a ds_read_b64_tr_b8 pass covers 8 rows {0-3, 8-11} (+4) and two
+// neighbouring chunk columns c, c+1 (c even). The 4 rows of each parity need
+// {c ^ f, c ^ f ^ 1} disjoint: f = 2 * ((r >> 1) & 1) + 4 * ((r >> 3) & 1).
+__device__ __forceinline__ int swz8_v(int r, int c) {
+  return r * 128 + ((c ^ ((((r >> 1) & 1) << 1) | (((r >> 3) & 1) << 2))) << 4);
 }
 
 __device__ __forceinline__ uint32_t pack_e4m3x4(float a, float b, float c, float d) {
@@ -129,8 +140,8 @@ void attn_fwd_fp8_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __restri
     for (int i = 0; i < C::kLoadsPerThread; ++i) {
       const int ci = tid + i * C::kThreads;
       const int r = ci / CH, c = ci % CH;
-      *(i32x4_t*)(kb + swz8<CH>(r, c)) = stK[i];
-      *(i32x4_t*)(vb + swz8<CH>(r, c)) = stV[i];
+      *(i32x4_t*)(kb + swz8_k(r, c)) = stK[i];
+      *(i32x4_t*)(vb + swz8_v(r, c)) = stV[i];
     }
   };
 
@@ -164,8 +175,8 @@ void attn_fwd_fp8_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __restri
 #pragma unroll
       for (int kb = 0; kb < KBLK; ++kb) {
         const int r = kb * 32 + l32;
-        const i32x4_t a0 = *(const i32x4_t*)(kbuf + swz8<CH>(r, ks * 4 + hh * 2));
-        const i32x4_t a1 = *(const i32x4_t*)(kbuf + swz8<CH>(r, ks * 4 + hh * 2 + 1));
+        const i32x4_t a0 = *(const i32x4_t*)(kbuf + swz8_k(r, ks * 4 + hh * 2));
+        const i32x4_t a1 = *(const i32x4_t*)(kbuf + swz8_k(r, ks * 4 + hh * 2 + 1));
         const i32x8_t a = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
@@ -247,7 +258,7 @@ void attn_fwd_fp8_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __restri
           const int key = kp * 64 + (u >> 1) * 32 + (u & 1) * 16 + tr_key;
           const int c = db * 2 + tr_chunk;
           const i32x2_t t = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-              DIT_LDS(i32x2_t, vbuf + swz8<CH>(key, c) + tr_off));
+              DIT_LDS(i32x2_t, vbuf + swz8_v(key, c) + tr_off));
           a[2 * u] = t[0];
           a[2 * u + 1] = t[1];
         }

@@ -21,9 +21,9 @@ constexpr int kMaxDevices = 64;
 std::atomic<int> g_device_state[kMaxDevices];
 
 // Kernel configurations. Rows per workgroup BR = NW * QB * 32.
-using CfgBf16D128 = Bf16Cfg<128, 1, 4, 64>;
-using CfgBf16D64 = Bf16Cfg<64, 2, 4, 64>;
-using CfgFp8D128 = Fp8Cfg<2, 4, 64>;
+using CfgBf16D128 = Bf16Cfg<128, 1, 8, 64, 2>;
+using CfgBf16D64 = Bf16Cfg<64, 1, 8, 64, 2>;
+using CfgFp8D128 = Fp8Cfg<1, 8, 128>;
 
 template <class C>
 hipError_t allow_lds_bf16() {
