@@ -1,92 +1,107 @@
-// bf16 attention forward for gfx950, software-pipelined, 64 query rows per wave.
+// bf16 attention forward for gfx950, d = 128: 64 query rows per wave,
+// software-pipelined, K/V tiles moved by LDS DMA.
 //
-// Why this shape. An MFMA operand read from LDS is reused once per 32-row
-// query block that the wave owns, so the LDS bytes read per flop fall as the
-// rows per wave grow. With 64 rows per wave (two 32-row blocks) the O
-// accumulator alone is 128 registers per lane, so one wave runs per SIMD and
-// the wave itself must keep the matrix cores busy. The loop is therefore
-// software-pipelined and explicitly interleaved:
+// Shape. A wave owns 64 query rows (two 32-row blocks), so every K or V
+// fragment it reads from LDS feeds two MFMAs; with 32 rows per wave the LDS
+// would have to deliver twice the bytes per flop. The O accumulator is then
+// 128 registers per lane and one wave runs per SIMD (4 waves, 256 rows per
+// workgroup), so the wave interleaves its own MFMA, VALU and LDS work.
 //
-// Iteration j (one tile of 32 keys) starts with S_j and its row maxima in
-// registers, K_{j+1} and V_j in LDS:
-//   [rare] raise the running maximum and rescale O, l
-//   read all K_{j+1} and V_j MFMA fragments from LDS (latency hidden by the
-//   first steps below); issue global loads of K_{j+2} and V_{j+1}
-//   phase A, one step per 16-wide d slice:  2 MFMAs of S_{j+1} = K_{j+1} Q^T
-//                                           + softmax of keys 0-15 of S_j
-//   phase B1, one step per 32-wide d block: 2 MFMAs of O^T += V_j^T P_j^T
-//                                           (keys 0-15) + softmax of keys 16-31
-//   phase B2, one step per 32-wide d block: 2 MFMAs (keys 16-31)
-//                                           + row maxima of S_{j+1}
-//   store K_{j+2}, V_{j+1} to LDS; barrier
-// Each step is fenced with a scheduling barrier, so the compiler keeps the
-// matrix-core and vector-ALU work of a step next to each other instead of
-// grouping all MFMAs and all VALU work. K_{j+2} overwrites K_j (last read in
-// iteration j-1) and V_{j+1} overwrites V_{j-1} (also read in iteration
-// j-1), so one barrier per tile suffices. The last two iterations are peeled
-// so the steady-state body has no branch other than the rare rescale.
+// Data movement. K and V tiles of 64 keys go from HBM to LDS with
+// buffer_load_dwordx4 ... lds: no staging registers, no LDS store
+// instructions, and rows past N arrive as zeros from the buffer range check.
+// Rows are padded (K 272 bytes, V 320 bytes) so that every fragment read is
+// free of bank conflicts and addressed by one register plus an immediate; the
+// DMA writes 1 KB of consecutive LDS per instruction, and lanes that land on
+// padding fetch a harmless in-tile chunk. K lives in a ring of 3 tile slots and
+// V in a ring of 2: tile u is computed on while K tile u+2 and V tile u+1
+// stream in, and one s_waitcnt + barrier per 64 keys publishes them.
 //
-// Layout conventions (S^T = K Q^T, O^T = V^T P^T, V^T via LDS transpose
-// reads, lazy rescaling) are those of the 32-row kernel in attn_fwd_bf16.h.
-// Built with -mllvm -amdgpu-mfma-vgpr-form so that the accumulators stay in
-// VGPRs and the rescale does not copy them between register files.
+// Sub-iteration j (32 keys), two phases of 16 MFMAs each:
+//   X: O^T += V_{j-1}^T P_{j-1}^T, interleaved with the exponent arguments of
+//      S_j's second query block and P_j = 2^t packed to bf16; the K_{j+1}
+//      fragment reads are issued first.
+//   Y: S_{j+1} = K_{j+1} Q^T (two chains of 8 MFMAs), interleaved with the row
+//      sums of P_j (v_dot2_f32_bf16 on the packed values), the exponent
+//      arguments of S_{j+1}'s first block and the V_j fragment reads.
+// P alternates between two register sets over the two sub-iterations of a
+// tile, so nothing is copied at the loop edge.
+//
+// Softmax without a per-tile maximum. The running maximum m (log2 units, per
+// query row) starts at the exact maximum of the first 32 keys and only moves
+// when a sub-tile's probabilities, relative to m, sum to more than 2^8 in
+// some lane. That rare path recomputes the sub-tile's logits from K (still in
+// LDS), takes their exact maximum, rescales O and l and recomputes P. Every
+// probability otherwise stays below 2^8. Row sums come from the bf16-rounded
+// probabilities, so each row of O is normalised by exactly the weights its
+// MFMAs used.
+// Layout conventions (S^T = K Q^T, O^T = V^T P^T, V^T by transpose reads)
+// are those of attn_fwd_bf16.h. Built with -mllvm -amdgpu-mfma-vgpr-form.
 #pragma once
 #include <type_traits>
 
 #include "attn_common.h"
-#include "attn_fwd_bf16.h"
 
 namespace ditattn {
 
-template <int D, int NW, int VSWZ = 2>
 struct PipeCfg {
-  static constexpr int kD = D, kNW = NW, kKB = 32, kQB = 2, kVSwz = VSWZ;
-  static constexpr int kThreads = NW * 64;
-  static constexpr int kBR = NW * 64;
-  static constexpr int kKS = D / 16;
-  static constexpr int kDB = D / 32;
-  static constexpr int kRowBytes = D * 2;
-  static constexpr int kChunks = kRowBytes / 16;
-  static constexpr int kTileBytes = kKB * kRowBytes;
-  static constexpr int kLdsBytes = 2 * 2 * kTileBytes;
-  static constexpr int kLoadsPerThread = kKB * kChunks / kThreads;
-  static_assert(kKB * kChunks % kThreads == 0, "tile chunks must split evenly over the workgroup");
-  static_assert(8 % kKS == 0 && 8 % kDB == 0, "softmax slices must split evenly over the steps");
+  static constexpr int kD = 128, kNW = 4, kThreads = 256, kBR = 256;
+  static constexpr int kKS = 8, kDB = 4;
+  static constexpr int kKRow = 272, kVRow = 320;          // padded row pitch in LDS (bytes)
+  static constexpr int kKTile = 64 * kKRow;               // 17408 bytes of K rows
+  static constexpr int kVTile = 64 * kVRow;               // 20480 bytes of V rows
+  // Both tiles move as 20 DMA instructions of 1 KB, 5 per wave, so every wave
+  // issues the same count; the last 3 K instructions land past the K rows, in
+  // the slot's slack, and read nothing (their offsets are past the tile).
+  static constexpr int kDmaPerWave = 5;
+  static constexpr int kSlot = kNW * kDmaPerWave * 1024;  // 20480
+  static constexpr int kKSlots = 4, kVSlots = 3;
+  static constexpr int kVBase = kKSlots * kSlot;
+  static constexpr int kLdsBytes = kVBase + kVSlots * kSlot;   // 143360
+  static_assert(kKTile <= kSlot && kVTile <= kSlot, "tile fits its slot");
 };
+
+constexpr float kPipeSumLimit = 256.0f;    // 2^8
 
 template <bool B>
 using flag_t = std::integral_constant<bool, B>;
 
-// Keep the instructions of one pipeline step together.
-#define DIT_STEP_FENCE() __builtin_amdgcn_sched_barrier(0)
+// 16 bytes per lane from a buffer into LDS at M0 + 16 * lane. Written as asm
+// so that the compiler does not order every later LDS read behind it (it
+// would wait for all loads in flight); completion is awaited explicitly with
+// s_waitcnt vmcnt before the barrier that publishes the tile.
+__device__ __forceinline__ void dma_b128(i32x4_t rsrc, int voffset, unsigned lds_addr) {
+  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voffset), "s"(rsrc), "{m0}"(lds_addr) : "memory");
+}
+
+#define DIT_FENCE() __builtin_amdgcn_sched_barrier(0)
 
 template <class C>
 __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void attn_fwd_bf16_pipe_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
                                const uint16_t* __restrict__ Vg, uint16_t* __restrict__ Og,
                                float* __restrict__ LSEg, int N, int n_qtiles, float scale_log2, float scale) {
-  constexpr int D = C::kD, QB = 2, KB = C::kKB, KS = C::kKS, DB = C::kDB;
-  constexpr int CH = C::kChunks, TB = C::kTileBytes, LPT = C::kLoadsPerThread;
+  constexpr int D = C::kD, KS = C::kKS, DB = C::kDB;
+  constexpr int KROW = C::kKRow, VROW = C::kVRow;
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  char* const kbuf0 = smem;               // K tiles: [2][TB]
-  char* const vbuf0 = smem + 2 * TB;      // V tiles: [2][TB]
 
   const int tile = xcd_remap(blockIdx.x, gridDim.x);
   const int bh = tile / n_qtiles;
   const int qt = tile - bh * n_qtiles;
   const size_t base = (size_t)bh * (size_t)N * D;
-  const uint16_t* Q = Qg + base;
-  const uint16_t* K = Kg + base;
-  const uint16_t* V = Vg + base;
+  const char* Kh = reinterpret_cast<const char*>(Kg + base);
+  const char* Vh = reinterpret_cast<const char*>(Vg + base);
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
   const int l32 = lane & 31, hh = lane >> 5;
   const int q0 = qt * C::kBR + wave * 64;
 
-  bf16x8_t qf[QB][KS];
+  bf16x8_t qf[2][KS];
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
+  for (int qb = 0; qb < 2; ++qb) {
+    const uint16_t* Q = Qg + base;
     const int row = q0 + qb * 32 + l32;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
@@ -96,242 +111,320 @@ void attn_fwd_bf16_pipe_kernel(const uint16_t* __restrict__ Qg, const uint16_t* 
     }
   }
 
-  f32x16_t acc[QB][DB];
+  const int n_t = (N + 63) / 64;          // 64-key tiles
+
+  // ---- DMA: instruction i of a tile writes LDS bytes [1024 i, 1024 i + 1024);
+  // lane L covers 16-byte slot 64 i + L of the padded tile
+  int kdo[C::kDmaPerWave], vdo[C::kDmaPerWave];
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb)
+  for (int m = 0; m < C::kDmaPerWave; ++m) {
+    const int s = 64 * (wave + 4 * m) + lane;
+    const int kr = s / (KROW / 16), kc = s % (KROW / 16);
+    const int vr = s / (VROW / 16), vc = s % (VROW / 16);
+    kdo[m] = kr * D * 2 + (kc < D / 8 ? kc * 16 : 0);
+    vdo[m] = vr * D * 2 + (vc < D / 8 ? vc * 16 : 0);
+  }
+  // buffer descriptor of one 64-key tile: the range check zero-fills rows past N
+  auto tile_rsrc = [&](const char* head, int t) __attribute__((always_inline)) {
+    const int rows = min(64, N - t * 64);
+    const unsigned long long a = (unsigned long long)(head + (size_t)t * 64 * D * 2);
+    i32x4_t rs;
+    rs[0] = __builtin_amdgcn_readfirstlane((int)(unsigned)a);
+    rs[1] = __builtin_amdgcn_readfirstlane((int)((a >> 32) & 0xffffu));   // stride 0
+    rs[2] = __builtin_amdgcn_readfirstlane(rows * D * 2);                   // bytes in range
+    rs[3] = 0x00020000;
+    return rs;
+  };
+  // the m-th DMA instruction of this wave for one tile (instruction wave + 4 m)
+  auto dma_one = [&](const i32x4_t& rs, const char* slot, const int (&off)[C::kDmaPerWave], int m)
+      __attribute__((always_inline)) {
+    const int i = wave + 4 * m;
+    dma_b128(rs, off[m], __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)DIT_LDS(const char, slot) + i * 1024));
+  };
+  auto dma_tile = [&](const char* head, int t, const char* slot, const int (&off)[C::kDmaPerWave])
+      __attribute__((always_inline)) {
+    const i32x4_t rs = tile_rsrc(head, t);
+#pragma unroll
+    for (int m = 0; m < C::kDmaPerWave; ++m) dma_one(rs, slot, off, m);
+  };
+  // Slot offsets pass through readfirstlane so that the compiler keeps them in
+  // an SGPR instead of folding the V base into every read's immediate offset,
+  // which exceeds the 16-bit field and costs a VALU add per read.
+  auto kslot = [&](int t) { return smem + __builtin_amdgcn_readfirstlane((t % C::kKSlots) * C::kSlot); };
+  auto vslot = [&](int t) {
+    return smem + __builtin_amdgcn_readfirstlane(C::kVBase + (t % C::kVSlots) * C::kSlot);
+  };
+
+  // ---- fragment reads
+  const int k_rd = l32 * KROW + hh * 16;
+  const int g = lane >> 4, gi = lane & 15;
+  const int v_rd = ((g >> 1) * 4 + (gi >> 2)) * VROW + (g & 1) * 32 + (gi & 3) * 8;
+  bf16x8_t kf[KS];
+  auto read_kfrags = [&](int j) {
+    const char* kb = kslot(j >> 1) + (j & 1) * 32 * KROW + k_rd;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) kf[ks] = __builtin_bit_cast(bf16x8_t, *(const i32x4_t*)(kb + ks * 32));
+  };
+  bf16x8_t vf[2][DB];
+  auto read_vfrags = [&](int j, int half) {
+    const char* vb = vslot(j >> 1) + (j & 1) * 32 * VROW + half * 16 * VROW + v_rd;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const char* p = vb + db * 64;
+      const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(DIT_LDS(i16x4_t, p));
+      const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(DIT_LDS(i16x4_t, (p + 8 * VROW)));
+      const i32x2_t lo2 = __builtin_bit_cast(i32x2_t, lo), hi2 = __builtin_bit_cast(i32x2_t, hi);
+      const i32x4_t a4 = {lo2[0], lo2[1], hi2[0], hi2[1]};
+      vf[half][db] = __builtin_bit_cast(bf16x8_t, a4);
+    }
+  };
+  // keys of sub-tile j past N do not exist
+  auto mask_keys = [&](int j, f32x16_t& s) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = j * 32 + (r >> 2) * 8 + hh * 4 + (r & 3);
+      s[r] = key < N ? s[r] : -INFINITY;
+    }
+  };
+  auto s_chain = [&](int qb, f32x16_t& s) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[r] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qf[qb][ks], s, 0, 0, 0);
+  };
+  auto row_max = [&](const f32x16_t& s) {
+    float mx = s[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
+    return pair_max(mx) * scale_log2;      // scale_log2 > 0
+  };
+  // P = 2^t for 8 consecutive entries of t, packed to bf16
+  auto exp_half = [&](const f32x16_t& t, int half, bf16x8_t& out) {
+    i32x4_t w;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const bf16x2_t pk = {(__bf16)fast_exp2(t[half * 8 + 2 * e]), (__bf16)fast_exp2(t[half * 8 + 2 * e + 1])};
+      w[e] = __builtin_bit_cast(int, pk);
+    }
+    out = __builtin_bit_cast(bf16x8_t, w);
+  };
+  const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
+  auto rowsum = [&](const bf16x8_t& p, float acc_s) {
+    const i32x4_t w = __builtin_bit_cast(i32x4_t, p);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      // the element goes through a scalar first: hipcc miscompiles a bit_cast
+      // whose operand is an element of an ext_vector (it reads element 0)
+      const int x = w[e];
+      acc_s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, x), ones, acc_s, false);
+    }
+    return acc_s;
+  };
+
+  f32x16_t acc[2][DB];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[qb][db][r] = 0.f;
-  float m_run[QB] = {-INFINITY, -INFINITY}, l_run[QB] = {0.f, 0.f};
-  float m_cur[QB];          // row maxima of the tile in s_cur
+  float mc[2];                 // running row maxima, log2 units
+  float l_run[2] = {0.f, 0.f};
+  f32x16_t t0;                 // exponent arguments of the current sub-tile, query block 0
+  f32x16_t s1;                 // raw logits of the current sub-tile, query block 1
+  bf16x8_t pA[2][2], pB[2][2]; // P of two consecutive sub-tiles [query block][key half]
 
-  const int n_kt = (N + KB - 1) / KB;
-
-  // ---- global -> register staging (rows past N read row N-1: they are masked or weighted 0)
-  auto gload = [&](const uint16_t* src, int kt, i32x4_t (&st)[LPT]) {
-#pragma unroll
-    for (int i = 0; i < LPT; ++i) {
-      const int ci = tid + i * C::kThreads;
-      const int r = ci / CH, c = ci % CH;
-      const int key = min(kt * KB + r, N - 1);
-      st[i] = *(const i32x4_t*)(src + (size_t)key * D + c * 8);
-    }
-  };
-  auto lstore_k = [&](char* dst, const i32x4_t (&st)[LPT]) {
-#pragma unroll
-    for (int i = 0; i < LPT; ++i) {
-      const int ci = tid + i * C::kThreads;
-      *(i32x4_t*)(dst + swz<CH>(ci / CH, ci % CH)) = st[i];
-    }
-  };
-  auto lstore_v = [&](char* dst, const i32x4_t (&st)[LPT]) {
-#pragma unroll
-    for (int i = 0; i < LPT; ++i) {
-      const int ci = tid + i * C::kThreads;
-      *(i32x4_t*)(dst + swz_v<CH, C::kVSwz>(ci / CH, ci % CH)) = st[i];
-    }
-  };
-  auto read_kfrags = [&](const char* kb_lds, bf16x8_t (&kf)[KS]) {
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      kf[ks] = __builtin_bit_cast(bf16x8_t, *(const i32x4_t*)(kb_lds + swz<CH>(l32, ks * 2 + hh)));
-  };
-
-  const int g = lane >> 4, gi = lane & 15;
-  const int tr_row = (g >> 1) * 4 + (gi >> 2);
-  const int tr_chunk = (g & 1) * 2 + ((gi & 3) >> 1);
-  const int tr_off = (gi & 1) * 8;
-  auto read_vfrags = [&](const char* vb, bf16x8_t (&vf)[2][DB]) {
-#pragma unroll
-    for (int half = 0; half < 2; ++half)
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const int rbase = half * 16 + tr_row;
-        const int c = db * 4 + tr_chunk;
-        const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            DIT_LDS(i16x4_t, (vb + swz_v<CH, C::kVSwz>(rbase, c) + tr_off)));
-        const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            DIT_LDS(i16x4_t, (vb + swz_v<CH, C::kVSwz>(rbase + 8, c) + tr_off)));
-        const i32x2_t lo2 = __builtin_bit_cast(i32x2_t, lo), hi2 = __builtin_bit_cast(i32x2_t, hi);
-        const i32x4_t a4 = {lo2[0], lo2[1], hi2[0], hi2[1]};
-        vf[half][db] = __builtin_bit_cast(bf16x8_t, a4);
-      }
-  };
-  auto mask_tail = [&](int kt, f32x16_t (&s)[QB]) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int key = kt * KB + (r >> 2) * 8 + hh * 4 + (r & 3);
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) s[qb][r] = key < N ? s[qb][r] : -INFINITY;
-    }
-  };
-
-  i32x4_t stK[LPT], stV[LPT];
-  // ---- prologue: K_0, V_0 -> buffer 0, K_1 -> buffer 1; S_0 and its row maxima
-  gload(K, 0, stK);
-  gload(V, 0, stV);
-  lstore_k(kbuf0, stK);
-  lstore_v(vbuf0, stV);
-  if (n_kt > 1) {
-    gload(K, 1, stK);
-    lstore_k(kbuf0 + TB, stK);
-  }
+  // ---- prologue: K tiles 0 and 1, V tile 0; S_0 and its exact row maxima
+  dma_tile(Kh, 0, kslot(0), kdo);
+  if (n_t > 1) dma_tile(Kh, 1, kslot(1), kdo);
+  if (n_t > 2) dma_tile(Kh, 2, kslot(2), kdo);
+  dma_tile(Vh, 0, vslot(0), vdo);
+  if (n_t > 1) dma_tile(Vh, 1, vslot(1), vdo);
+  __builtin_amdgcn_s_waitcnt(0x0F70);      // vmcnt(0)
   __syncthreads();
-  f32x16_t s_cur[QB];
+  read_kfrags(0);
   {
-    bf16x8_t kf[KS];
-    read_kfrags(kbuf0, kf);
+    f32x16_t s0;
+    s_chain(0, s0);
+    s_chain(1, s1);
+    if (N < 32) { mask_keys(0, s0); mask_keys(0, s1); }
+    mc[0] = row_max(s0);
+    mc[1] = row_max(s1);
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
+    for (int r = 0; r < 16; ++r) t0[r] = fmaf(s0[r], scale_log2, -mc[0]);
+  }
+  // the first phase X adds 0 * 0: no previous sub-tile yet
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s_cur[qb][r] = 0.f;
+  for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        s_cur[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qf[qb][ks], s_cur[qb], 0, 0, 0);
+    for (int x = 0; x < 2; ++x) pA[h][x] = bf16x8_t{};
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int db = 0; db < DB; ++db) vf[h][db] = bf16x8_t{};
+
+  // One sub-iteration: consumes P_{j-1} (pin), produces P_j (pout).
+  // MASK: keys of S_{j+1} (and, on the rare path, of S_j) may lie past N.
+  // dma(st) issues this sub-iteration's share of the tile DMA at phase-Y step st.
+  auto sub = [&](int j, bf16x8_t (&pin)[2][2], bf16x8_t (&pout)[2][2], auto mask_c, auto&& dma)
+      __attribute__((always_inline)) {
+    constexpr bool MASK = decltype(mask_c)::value;
+    // ================= phase X
+    read_kfrags(j + 1);
+    DIT_FENCE();
+    {
+      const float m1 = mc[1];
+      f32x16_t& t1 = s1;       // in place
+#pragma unroll
+      for (int st = 0; st < 8; ++st) {
+        const int half = st >> 2, db = st & 3;
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+          acc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[half][db], pin[qb][half], acc[qb][db], 0, 0, 0);
+        if (st < 4) {
+#pragma unroll
+          for (int r = st * 4; r < st * 4 + 4; ++r) t1[r] = fmaf(s1[r], scale_log2, -m1);
+        }
+        if (st == 1) exp_half(t0, 0, pout[0][0]);
+        if (st == 3) exp_half(t0, 1, pout[0][1]);
+        if (st == 5) exp_half(t1, 0, pout[1][0]);
+        if (st == 7) exp_half(t1, 1, pout[1][1]);
+        DIT_FENCE();
+      }
     }
-  }
-  if (n_kt == 1) mask_tail(0, s_cur);
+    // ================= phase Y
+    float ls0 = 0.f, ls1 = 0.f;
+    {
+      f32x16_t sa, sb;
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    float m = s_cur[qb][0];
+      for (int r = 0; r < 16; ++r) { sa[r] = 0.f; sb[r] = 0.f; }
+      // steps 0-3: S_{j+1} of query block 0, with the row sums of P_j
 #pragma unroll
-    for (int r = 1; r < 16; ++r) m = fmaxf(m, s_cur[qb][r]);
-    m_cur[qb] = pair_max(m);
-  }
-  __syncthreads();
-
-  // One pipelined iteration. NEXT: compute S_{kt+1}; MASK: it is the last tile and
-  // may be partial; LOADK / LOADV: fetch K_{kt+2} / V_{kt+1}.
-  auto iteration = [&](int kt, auto next_t, auto mask_t, auto loadk_t, auto loadv_t) {
-    constexpr bool NEXT = decltype(next_t)::value, MASK = decltype(mask_t)::value;
-    constexpr bool LOADK = decltype(loadk_t)::value, LOADV = decltype(loadv_t)::value;
-
-    // [rare] the running maximum grows by more than TAU: rescale O and l
-    bool grow = false;
+      for (int st = 0; st < 4; ++st) {
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) grow |= (m_cur[qb] - m_run[qb]) * scale_log2 > kTauBf16;
-    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+        for (int k2 = 0; k2 < 2; ++k2)
+          sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[st * 2 + k2], qf[0][st * 2 + k2], sa, 0, 0, 0);
+        // the V_j fragment reads go behind the first MFMAs, which then wait
+        // for nothing (the K fragments were read a phase earlier); at most 8
+        // at a time, since lgkmcnt counts no more than 15 outstanding reads
+        if (st < 2) {
+          DIT_FENCE();
+          read_vfrags(j, st);
+          DIT_FENCE();
+        }
+        if (st == 0) ls0 = rowsum(pout[0][0], ls0);
+        if (st == 1) ls0 = rowsum(pout[0][1], ls0);
+        if (st == 2) ls1 = rowsum(pout[1][0], ls1);
+        if (st == 3) ls1 = rowsum(pout[1][1], ls1);
+        DIT_FENCE();
+      }
+      if constexpr (MASK) {
+        if (32 * (j + 2) > N) mask_keys(j + 1, sa);
+      }
+      const float m0 = mc[0];
+      // steps 4-7: query block 1, with the exponent arguments of block 0
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        const float m_new = fmaxf(m_run[qb], m_cur[qb]);
-        const float alpha = fast_exp2((m_run[qb] - m_new) * scale_log2);
+      for (int st = 0; st < 4; ++st) {
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2)
+          sb = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[st * 2 + k2], qf[1][st * 2 + k2], sb, 0, 0, 0);
+#pragma unroll
+        for (int r = st * 4; r < st * 4 + 4; ++r) t0[r] = fmaf(sa[r], scale_log2, -m0);
+        dma(st);
+        DIT_FENCE();
+      }
+      if constexpr (MASK) {
+        if (32 * (j + 2) > N) mask_keys(j + 1, sb);
+      }
+      s1 = sb;
+    }
+    // ---- rare path: a probability of sub-tile j exceeded 2^8
+    const bool bad = !(ls0 <= kPipeSumLimit) || !(ls1 <= kPipeSumLimit);
+    if (__builtin_amdgcn_ballot_w64(bad) != 0) {
+      read_kfrags(j);                      // K tile j/2 is still in its slot
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        f32x16_t s;
+        s_chain(qb, s);
+        if constexpr (MASK) {
+          if (32 * (j + 1) > N) mask_keys(j, s);
+        }
+        const float m_new = fmaxf(mc[qb], row_max(s));
+        const float alpha = fast_exp2(mc[qb] - m_new);
         l_run[qb] *= alpha;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
           for (int r = 0; r < 16; ++r) acc[qb][db][r] *= alpha;
-        m_run[qb] = m_new;
+        if (qb == 0) {
+          const float shift = m_new - mc[0];
+#pragma unroll
+          for (int r = 0; r < 16; ++r) t0[r] -= shift;    // S_{j+1}'s arguments used the old maximum
+        }
+        mc[qb] = m_new;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[r] = fmaf(s[r], scale_log2, -m_new);
+        exp_half(s, 0, pout[qb][0]);
+        exp_half(s, 1, pout[qb][1]);
       }
+      ls0 = rowsum(pout[0][1], rowsum(pout[0][0], 0.f));
+      ls1 = rowsum(pout[1][1], rowsum(pout[1][0], 0.f));
     }
-    DIT_STEP_FENCE();
-
-    // fragment reads for this iteration, then the global loads of later tiles
-    bf16x8_t kf[KS];
-    if constexpr (NEXT) read_kfrags(kbuf0 + ((kt + 1) & 1) * TB, kf);
-    bf16x8_t vf[2][DB];
-    read_vfrags(vbuf0 + (kt & 1) * TB, vf);
-    if constexpr (LOADK) gload(K, kt + 2, stK);
-    if constexpr (LOADV) gload(V, kt + 1, stV);
-    DIT_STEP_FENCE();
-
-    const float mc0 = m_run[0] * scale_log2, mc1 = m_run[1] * scale_log2;
-    float ls0 = 0.f, ls1 = 0.f;
-    float p[QB][16];
-    auto softmax_slice = [&](int r0, int nr) {
-#pragma unroll
-      for (int r = r0; r < r0 + nr; ++r) {
-        p[0][r] = fast_exp2(fmaf(s_cur[0][r], scale_log2, -mc0));
-        p[1][r] = fast_exp2(fmaf(s_cur[1][r], scale_log2, -mc1));
-        ls0 += p[0][r];
-        ls1 += p[1][r];
-      }
-    };
-    auto pack_p = [&](int half, bf16x8_t (&pb)[QB]) {
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        bf16x8_t v;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = (__bf16)p[qb][half * 8 + e];
-        pb[qb] = v;
-      }
-    };
-
-    // ---- phase A: S_{j+1} (MFMA) with the softmax of keys 0-15 of S_j (VALU)
-    f32x16_t s_nxt[QB];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s_nxt[qb][r] = 0.f;
-    constexpr int kSliceA = 8 / KS;      // elements per qb per phase-A step (keys 0-15: regs 0-7)
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      if constexpr (NEXT) {
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
-          s_nxt[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qf[qb][ks], s_nxt[qb], 0, 0, 0);
-      }
-      softmax_slice(ks * kSliceA, kSliceA);
-      DIT_STEP_FENCE();
-    }
-    bf16x8_t pb0[QB], pb1[QB];
-    pack_p(0, pb0);
-
-    // ---- phase B1: O^T += V^T P^T for keys 0-15 (MFMA) with the softmax of keys 16-31
-    constexpr int kSliceB = 8 / DB;
-#pragma unroll
-    for (int db = 0; db < DB; ++db) {
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb)
-        acc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[0][db], pb0[qb], acc[qb][db], 0, 0, 0);
-      softmax_slice(8 + db * kSliceB, kSliceB);
-      DIT_STEP_FENCE();
-    }
-    pack_p(1, pb1);
     l_run[0] += ls0;
     l_run[1] += ls1;
-
-    // ---- phase B2: keys 16-31 (MFMA) with the row maxima of S_{j+1} (VALU)
-    if constexpr (NEXT && MASK) mask_tail(kt + 1, s_nxt);
-    float mx0 = -INFINITY, mx1 = -INFINITY;
-#pragma unroll
-    for (int db = 0; db < DB; ++db) {
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb)
-        acc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[1][db], pb1[qb], acc[qb][db], 0, 0, 0);
-      if constexpr (NEXT) {
-        constexpr int kSliceM = 16 / DB;
-#pragma unroll
-        for (int r = db * kSliceM; r < (db + 1) * kSliceM; ++r) {
-          mx0 = fmaxf(mx0, s_nxt[0][r]);
-          mx1 = fmaxf(mx1, s_nxt[1][r]);
-        }
-      }
-      DIT_STEP_FENCE();
-    }
-    if constexpr (NEXT) {
-      m_cur[0] = pair_max(mx0);
-      m_cur[1] = pair_max(mx1);
-      s_cur[0] = s_nxt[0];
-      s_cur[1] = s_nxt[1];
-    }
-    if constexpr (LOADK) lstore_k(kbuf0 + (kt & 1) * TB, stK);
-    if constexpr (LOADV) lstore_v(vbuf0 + ((kt + 1) & 1) * TB, stV);
-    __syncthreads();
   };
 
-  using T = flag_t<true>;
-  using F = flag_t<false>;
-  int kt = 0;
-  for (; kt + 2 < n_kt; ++kt) iteration(kt, T{}, F{}, T{}, T{});
-  if (kt + 1 < n_kt) {          // second to last: S of the last tile, which may be partial
-    iteration(kt, T{}, T{}, F{}, T{});
-    ++kt;
-  }
-  iteration(kt, F{}, F{}, F{}, F{});
+  // One 64-key tile u. It streams in K tile u+3 (during its first
+  // sub-iteration) and V tile u+2 (during its second), one DMA instruction per
+  // phase-Y step, and then waits for the tiles issued one iteration earlier
+  // (K u+2, V u+1) before the barrier that publishes them. In the steady
+  // state (TAIL false) both DMAs exist and no key of tiles u, u+1 lies past N,
+  // so the body has no branch but the rare path: a branch would let the
+  // compiler sink the softmax work out of the MFMA phases.
+  auto iteration = [&](int u, auto tail_c) __attribute__((always_inline)) {
+    constexpr bool TAIL = decltype(tail_c)::value;
+    const bool k_next = !TAIL || u + 3 < n_t, v_next = !TAIL || u + 2 < n_t;
+    const i32x4_t rk = tile_rsrc(Kh, u + 3), rv = tile_rsrc(Vh, u + 2);
+    const char* sk = kslot(u + 3);
+    const char* sv = vslot(u + 2);
+    DIT_FENCE();
+    // hook steps st = 0..3 issue instructions m = st, and m = 4 at st = 0
+    static_assert(C::kDmaPerWave == 5, "DMA hook spreads 5 instructions over 4 steps");
+    sub(2 * u, pA, pB, tail_c, [&](int st) __attribute__((always_inline)) {
+      if (k_next) {
+        dma_one(rk, sk, kdo, st);
+        if (st == 0) dma_one(rk, sk, kdo, 4);
+      }
+    });
+    sub(2 * u + 1, pB, pA, tail_c, [&](int st) __attribute__((always_inline)) {
+      if (v_next) {
+        dma_one(rv, sv, vdo, st);
+        if (st == 0) dma_one(rv, sv, vdo, 4);
+      }
+    });
+    DIT_FENCE();
+    if (TAIL)
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    else
+      __builtin_amdgcn_s_waitcnt(0x0F7A);  // vmcnt(10): this iteration's 10 DMAs may stay in flight
+    __syncthreads();
+    DIT_FENCE();
+  };
+  int u = 0;
+  for (; u + 3 < n_t; ++u) iteration(u, flag_t<false>{});
+  for (; u < n_t; ++u) iteration(u, flag_t<true>{});
+
+  // ---- P V of the last sub-tile (its V fragments were read in the last phase Y)
+#pragma unroll
+  for (int half = 0; half < 2; ++half)
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+        acc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[half][db], pA[qb][half], acc[qb][db], 0, 0, 0);
 
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
+  for (int qb = 0; qb < 2; ++qb) {
     const float l_tot = pair_sum(l_run[qb]);
     const float inv = 1.0f / l_tot;
     const int row = q0 + qb * 32 + l32;
@@ -347,11 +440,12 @@ void attn_fwd_bf16_pipe_kernel(const uint16_t* __restrict__ Qg, const uint16_t* 
           w.y = pack_bf16x2(acc[qb][db][i * 4 + 2] * inv, acc[qb][db][i * 4 + 3] * inv);
           *(uint2*)(orow + d0) = w;
         }
-      if (LSEg != nullptr && hh == 0) LSEg[(size_t)bh * N + row] = m_run[qb] * scale + logf(l_tot);
+      if (LSEg != nullptr && hh == 0)
+        LSEg[(size_t)bh * N + row] = (mc[qb] + __log2f(l_tot)) * 0.6931471805599453f;
     }
   }
 }
 
-#undef DIT_STEP_FENCE
+#undef DIT_FENCE
 
 }  // namespace ditattn

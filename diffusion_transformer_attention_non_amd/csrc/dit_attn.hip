@@ -9,6 +9,7 @@
 
 #include "dit_attn.h"
 #include "attn_fwd_bf16.h"
+#include "attn_fwd_bf16_pipe.h"
 #include "attn_fwd_fp8.h"
 #include "quant_e4m3.h"
 
@@ -20,14 +21,21 @@ constexpr int kMaxDevices = 64;
 // 0 = not checked yet, 1 = gfx950 and kernels configured, 2 = unsupported device
 std::atomic<int> g_device_state[kMaxDevices];
 
-// Kernel configurations. Rows per workgroup BR = NW * QB * 32.
-using CfgBf16D128 = Bf16Cfg<128, 1, 8, 64, 2>;
+// Kernel configurations. bf16 d = 128 runs the 64-rows-per-wave pipelined
+// kernel (256 rows per workgroup); d = 64 the 32-rows-per-wave kernel with
+// BR = NW * QB * 32 rows per workgroup.
+using CfgBf16D128 = PipeCfg;
 using CfgBf16D64 = Bf16Cfg<64, 1, 8, 64, 2>;
 using CfgFp8D128 = Fp8Cfg<1, 8, 128>;
 
 template <class C>
 hipError_t allow_lds_bf16() {
   return hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_fwd_bf16_kernel<C>),
+                             hipFuncAttributeMaxDynamicSharedMemorySize, C::kLdsBytes);
+}
+template <class C>
+hipError_t allow_lds_pipe() {
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_fwd_bf16_pipe_kernel<C>),
                              hipFuncAttributeMaxDynamicSharedMemorySize, C::kLdsBytes);
 }
 template <class C>
@@ -46,7 +54,7 @@ int check_device() {
   if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return DIT_ATTN_EDEVICE;
   const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
   if (ok) {
-    if (allow_lds_bf16<CfgBf16D128>() != hipSuccess || allow_lds_bf16<CfgBf16D64>() != hipSuccess ||
+    if (allow_lds_pipe<CfgBf16D128>() != hipSuccess || allow_lds_bf16<CfgBf16D64>() != hipSuccess ||
         allow_lds_fp8<CfgFp8D128>() != hipSuccess)
       return DIT_ATTN_EDEVICE;
   }
@@ -69,6 +77,20 @@ int launch_bf16(const void* q, const void* k, const void* v, void* o, float* lse
   if (grid > 0x7fffffffLL) return DIT_ATTN_EINVAL;
   const float scale_log2 = scale * 1.4426950408889634f;
   hipLaunchKernelGGL(attn_fwd_bf16_kernel<C>, dim3((unsigned)grid), dim3(C::kThreads), C::kLdsBytes, st,
+                     static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                     static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), lse, N, n_qtiles,
+                     scale_log2, scale);
+  return hipGetLastError() == hipSuccess ? DIT_ATTN_OK : DIT_ATTN_ELAUNCH;
+}
+
+template <class C>
+int launch_pipe(const void* q, const void* k, const void* v, void* o, float* lse, int BH, int N,
+                float scale, hipStream_t st) {
+  const int n_qtiles = (N + C::kBR - 1) / C::kBR;
+  const long long grid = (long long)n_qtiles * BH;
+  if (grid > 0x7fffffffLL) return DIT_ATTN_EINVAL;
+  const float scale_log2 = scale * 1.4426950408889634f;
+  hipLaunchKernelGGL(attn_fwd_bf16_pipe_kernel<C>, dim3((unsigned)grid), dim3(C::kThreads), C::kLdsBytes, st,
                      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                      static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), lse, N, n_qtiles,
                      scale_log2, scale);
@@ -137,7 +159,7 @@ int dit_attn_fwd_ex(const void* q, const void* k, const void* v, void* o, int B,
   if (dev_status != DIT_ATTN_OK) return dev_status;
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (dtype == DIT_ATTN_BF16) {
-    if (d == 128) return launch_bf16<CfgBf16D128>(q, k, v, o, lse, (int)bh, N, scale, st);
+    if (d == 128) return launch_pipe<CfgBf16D128>(q, k, v, o, lse, (int)bh, N, scale, st);
     return launch_bf16<CfgBf16D64>(q, k, v, o, lse, (int)bh, N, scale, st);
   }
   return launch_fp8<CfgFp8D128>(q, k, v, o, lse, descale_qkv, (int)bh, N, scale, st);
