@@ -63,6 +63,18 @@ struct PipeCfg {
 
 constexpr float kPipeSumLimit = 256.0f;    // 2^8
 
+// Key-range split of the last, partly filled round of workgroups. The first
+// n_full workgroups each take one 256-row query tile over all keys. The next
+// n_split * parts workgroups take the remaining n_split query tiles, each
+// split into `parts` contiguous ranges of 64-key tiles; they write their rows
+// normalised over their own keys (fp32, ws_o) with the log2-sum-exp of that
+// range (ws_lse), and attn_split_combine_kernel merges the parts.
+struct PipeSplit {
+  int n_full, n_split, parts;
+  float* ws_o;      // [n_split * parts][256][128]
+  float* ws_lse;    // [n_split * parts][256], log2 units
+};
+
 template <bool B>
 using flag_t = std::integral_constant<bool, B>;
 
@@ -80,12 +92,27 @@ template <class C>
 __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void attn_fwd_bf16_pipe_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
                                const uint16_t* __restrict__ Vg, uint16_t* __restrict__ Og,
-                               float* __restrict__ LSEg, int N, int n_qtiles, float scale_log2, float scale) {
+                               float* __restrict__ LSEg, int N, int n_qtiles, float scale_log2, float scale,
+                               PipeSplit split) {
   constexpr int D = C::kD, KS = C::kKS, DB = C::kDB;
   constexpr int KROW = C::kKRow, VROW = C::kVRow;
   extern __shared__ __attribute__((aligned(16))) char smem[];
 
-  const int tile = xcd_remap(blockIdx.x, gridDim.x);
+  const int n_t = (N + 63) / 64;          // 64-key tiles
+  // query tile and key-tile range [u0, u1) of this workgroup
+  int tile, u0 = 0, u1 = n_t, ws_index = -1;
+  if ((int)blockIdx.x < split.n_full) {
+    tile = xcd_remap(blockIdx.x, split.n_full);
+  } else {
+    // neighbouring indices (one XCD) share a key range: K/V reuse in L2
+    const int sidx = xcd_remap(blockIdx.x - split.n_full, gridDim.x - split.n_full);
+    const int part = sidx / split.n_split;
+    const int ti = sidx - part * split.n_split;
+    tile = split.n_full + ti;
+    u0 = part * n_t / split.parts;
+    u1 = (part + 1) * n_t / split.parts;
+    ws_index = part * split.n_split + ti;
+  }
   const int bh = tile / n_qtiles;
   const int qt = tile - bh * n_qtiles;
   const size_t base = (size_t)bh * (size_t)N * D;
@@ -110,8 +137,6 @@ void attn_fwd_bf16_pipe_kernel(const uint16_t* __restrict__ Qg, const uint16_t* 
       qf[qb][ks] = __builtin_bit_cast(bf16x8_t, raw);
     }
   }
-
-  const int n_t = (N + 63) / 64;          // 64-key tiles
 
   // ---- DMA: instruction i of a tile writes LDS bytes [1024 i, 1024 i + 1024);
   // lane L covers 16-byte slot 64 i + L of the padded tile
@@ -234,20 +259,21 @@ void attn_fwd_bf16_pipe_kernel(const uint16_t* __restrict__ Qg, const uint16_t* 
   f32x16_t s1;                 // raw logits of the current sub-tile, query block 1
   bf16x8_t pA[2][2], pB[2][2]; // P of two consecutive sub-tiles [query block][key half]
 
-  // ---- prologue: K tiles 0 and 1, V tile 0; S_0 and its exact row maxima
-  dma_tile(Kh, 0, kslot(0), kdo);
-  if (n_t > 1) dma_tile(Kh, 1, kslot(1), kdo);
-  if (n_t > 2) dma_tile(Kh, 2, kslot(2), kdo);
-  dma_tile(Vh, 0, vslot(0), vdo);
-  if (n_t > 1) dma_tile(Vh, 1, vslot(1), vdo);
+  // ---- prologue: K tiles u0..u0+2, V tiles u0, u0+1; the first sub-tile's
+  // logits and their exact row maxima
+  dma_tile(Kh, u0, kslot(u0), kdo);
+  if (u0 + 1 < u1) dma_tile(Kh, u0 + 1, kslot(u0 + 1), kdo);
+  if (u0 + 2 < u1) dma_tile(Kh, u0 + 2, kslot(u0 + 2), kdo);
+  dma_tile(Vh, u0, vslot(u0), vdo);
+  if (u0 + 1 < u1) dma_tile(Vh, u0 + 1, vslot(u0 + 1), vdo);
   __builtin_amdgcn_s_waitcnt(0x0F70);      // vmcnt(0)
   __syncthreads();
-  read_kfrags(0);
+  read_kfrags(2 * u0);
   {
     f32x16_t s0;
     s_chain(0, s0);
     s_chain(1, s1);
-    if (N < 32) { mask_keys(0, s0); mask_keys(0, s1); }
+    if (32 * (2 * u0 + 1) > N) { mask_keys(2 * u0, s0); mask_keys(2 * u0, s1); }
     mc[0] = row_max(s0);
     mc[1] = row_max(s1);
 #pragma unroll
@@ -383,7 +409,7 @@ void attn_fwd_bf16_pipe_kernel(const uint16_t* __restrict__ Qg, const uint16_t* 
   // compiler sink the softmax work out of the MFMA phases.
   auto iteration = [&](int u, auto tail_c) __attribute__((always_inline)) {
     constexpr bool TAIL = decltype(tail_c)::value;
-    const bool k_next = !TAIL || u + 3 < n_t, v_next = !TAIL || u + 2 < n_t;
+    const bool k_next = !TAIL || u + 3 < u1, v_next = !TAIL || u + 2 < u1;
     const i32x4_t rk = tile_rsrc(Kh, u + 3), rv = tile_rsrc(Vh, u + 2);
     const char* sk = kslot(u + 3);
     const char* sv = vslot(u + 2);
@@ -410,9 +436,11 @@ void attn_fwd_bf16_pipe_kernel(const uint16_t* __restrict__ Qg, const uint16_t* 
     __syncthreads();
     DIT_FENCE();
   };
-  int u = 0;
-  for (; u + 3 < n_t; ++u) iteration(u, flag_t<false>{});
-  for (; u < n_t; ++u) iteration(u, flag_t<true>{});
+  // Sub-tiles past u1 that the pipeline touches (S of sub-tile 2 u1) read a
+  // slot that is stale or zero: their values are never used.
+  int u = u0;
+  for (; u + 3 < u1; ++u) iteration(u, flag_t<false>{});
+  for (; u < u1; ++u) iteration(u, flag_t<true>{});
 
   // ---- P V of the last sub-tile (its V fragments were read in the last phase Y)
 #pragma unroll
@@ -423,6 +451,27 @@ void attn_fwd_bf16_pipe_kernel(const uint16_t* __restrict__ Qg, const uint16_t* 
       for (int qb = 0; qb < 2; ++qb)
         acc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[half][db], pA[qb][half], acc[qb][db], 0, 0, 0);
 
+  if (ws_index >= 0) {
+    // one key range of a split tile: fp32 rows normalised over the range
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      const float l_tot = pair_sum(l_run[qb]);
+      const float inv = 1.0f / l_tot;
+      const int r = wave * 64 + qb * 32 + l32;
+      float* orow = split.ws_o + ((size_t)ws_index * C::kBR + r) * D;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int d0 = db * 32 + i * 8 + hh * 4;
+          f32x4_t w = {acc[qb][db][i * 4 + 0] * inv, acc[qb][db][i * 4 + 1] * inv, acc[qb][db][i * 4 + 2] * inv,
+                       acc[qb][db][i * 4 + 3] * inv};
+          *(f32x4_t*)(orow + d0) = w;
+        }
+      if (hh == 0) split.ws_lse[(size_t)ws_index * C::kBR + r] = mc[qb] + __log2f(l_tot);
+    }
+    return;
+  }
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     const float l_tot = pair_sum(l_run[qb]);
@@ -447,5 +496,39 @@ void attn_fwd_bf16_pipe_kernel(const uint16_t* __restrict__ Qg, const uint16_t* 
 }
 
 #undef DIT_FENCE
+
+// Merges the key-range parts of the split query tiles: per row,
+// O = sum_p w_p O_p / sum_p w_p with w_p = 2^(lse_p - max_p lse_p). Eight
+// rows per 256-thread block, four d values per thread.
+__global__ __launch_bounds__(256) void attn_split_combine_kernel(const float* __restrict__ ws_o,
+                                                                 const float* __restrict__ ws_lse,
+                                                                 uint16_t* __restrict__ Og, float* __restrict__ LSEg,
+                                                                 int N, int n_qtiles, PipeSplit split) {
+  constexpr int D = PipeCfg::kD, BR = PipeCfg::kBR;
+  const int ti = blockIdx.x / (BR / 8);
+  const int r = (blockIdx.x % (BR / 8)) * 8 + (threadIdx.x >> 5);
+  const int c = (threadIdx.x & 31) * 4;
+  const int tile = split.n_full + ti;
+  const int bh = tile / n_qtiles, qt = tile - bh * n_qtiles;
+  const int row = qt * BR + r;
+  if (row >= N) return;
+  float mx = -INFINITY;
+  for (int p = 0; p < split.parts; ++p) mx = fmaxf(mx, ws_lse[(size_t)(p * split.n_split + ti) * BR + r]);
+  float wsum = 0.f;
+  f32x4_t o = {0.f, 0.f, 0.f, 0.f};
+  for (int p = 0; p < split.parts; ++p) {
+    const size_t idx = (size_t)(p * split.n_split + ti) * BR + r;
+    const float w = fast_exp2(ws_lse[idx] - mx);
+    wsum += w;
+    const f32x4_t x = *(const f32x4_t*)(ws_o + idx * D + c);
+    o += w * x;
+  }
+  const float inv = 1.0f / wsum;
+  uint2 out;
+  out.x = pack_bf16x2(o[0] * inv, o[1] * inv);
+  out.y = pack_bf16x2(o[2] * inv, o[3] * inv);
+  *(uint2*)(Og + ((size_t)bh * N + row) * D + c) = out;
+  if (LSEg != nullptr && c == 0) LSEg[(size_t)bh * N + row] = (mx + __log2f(wsum)) * 0.6931471805599453f;
+}
 
 }  // namespace ditattn

@@ -2,6 +2,7 @@
 // kernel selection and launch on the caller's stream.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cmath>
 #include <cstdint>
@@ -20,6 +21,8 @@ namespace {
 constexpr int kMaxDevices = 64;
 // 0 = not checked yet, 1 = gfx950 and kernels configured, 2 = unsupported device
 std::atomic<int> g_device_state[kMaxDevices];
+// compute units per device (set with the device state)
+int g_num_cu[kMaxDevices];
 
 // Kernel configurations. bf16 d = 128 runs the 64-rows-per-wave pipelined
 // kernel (256 rows per workgroup); d = 64 the 32-rows-per-wave kernel with
@@ -58,8 +61,20 @@ int check_device() {
         allow_lds_fp8<CfgFp8D128>() != hipSuccess)
       return DIT_ATTN_EDEVICE;
   }
+  if (ok && dev < kMaxDevices) {
+    int n_cu = 0;
+    if (hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n_cu <= 0)
+      return DIT_ATTN_EDEVICE;
+    g_num_cu[dev] = n_cu;
+  }
   if (dev < kMaxDevices) g_device_state[dev].store(ok ? 1 : 2, std::memory_order_release);
   return ok ? DIT_ATTN_OK : DIT_ATTN_EDEVICE;
+}
+
+int cu_count() {
+  int dev = 0;
+  (void)hipGetDevice(&dev);
+  return dev >= 0 && dev < kMaxDevices && g_num_cu[dev] > 0 ? g_num_cu[dev] : 256;
 }
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
@@ -83,18 +98,62 @@ int launch_bf16(const void* q, const void* k, const void* v, void* o, float* lse
   return hipGetLastError() == hipSuccess ? DIT_ATTN_OK : DIT_ATTN_ELAUNCH;
 }
 
+// One workgroup (256 query rows) runs per CU, so a grid of T tiles takes
+// ceil(T / n_cu) rounds and the last round holds rem = T mod n_cu tiles. Those
+// are split into `parts` key ranges (rem * parts <= n_cu, at least 4 key tiles
+// per range) that run side by side; a combine kernel merges them. The fp32
+// partial rows live in a stream-ordered allocation freed after the combine.
+// Returns 0 (no split) when the last round is full or more than half full,
+// or when the partial buffers cannot be had.
+int plan_split(int BH, int n_qtiles, int N, int n_cu, PipeSplit* sp) {
+  *sp = PipeSplit{BH * n_qtiles, 0, 1, nullptr, nullptr};
+  const int tiles = BH * n_qtiles;
+  const int rem = tiles % n_cu;
+  const int n_t = (N + 63) / 64;
+  if (rem == 0) return 0;
+  const int parts = std::min(n_cu / rem, n_t / 4);
+  if (parts < 2) return 0;
+  sp->n_full = tiles - rem;
+  sp->n_split = rem;
+  sp->parts = parts;
+  return 1;
+}
+
 template <class C>
 int launch_pipe(const void* q, const void* k, const void* v, void* o, float* lse, int BH, int N,
-                float scale, hipStream_t st) {
+                float scale, hipStream_t st, int n_cu) {
   const int n_qtiles = (N + C::kBR - 1) / C::kBR;
-  const long long grid = (long long)n_qtiles * BH;
-  if (grid > 0x7fffffffLL) return DIT_ATTN_EINVAL;
+  const long long tiles = (long long)n_qtiles * BH;
+  if (tiles > 0x7fffffffLL / 8) return DIT_ATTN_EINVAL;
   const float scale_log2 = scale * 1.4426950408889634f;
+  PipeSplit sp;
+  void* ws = nullptr;
+  if (plan_split(BH, n_qtiles, N, n_cu, &sp)) {
+    const size_t units = (size_t)sp.n_split * sp.parts * C::kBR;
+    if (hipMallocAsync(&ws, units * (C::kD + 1) * sizeof(float), st) == hipSuccess && ws != nullptr) {
+      sp.ws_o = static_cast<float*>(ws);
+      sp.ws_lse = sp.ws_o + units * C::kD;
+    } else {
+      (void)hipGetLastError();
+      ws = nullptr;
+      sp = PipeSplit{(int)tiles, 0, 1, nullptr, nullptr};
+    }
+  }
+  const long long grid = (long long)sp.n_full + (long long)sp.n_split * sp.parts;
   hipLaunchKernelGGL(attn_fwd_bf16_pipe_kernel<C>, dim3((unsigned)grid), dim3(C::kThreads), C::kLdsBytes, st,
                      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                      static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), lse, N, n_qtiles,
-                     scale_log2, scale);
-  return hipGetLastError() == hipSuccess ? DIT_ATTN_OK : DIT_ATTN_ELAUNCH;
+                     scale_log2, scale, sp);
+  hipError_t err = hipGetLastError();
+  if (ws != nullptr) {
+    if (err == hipSuccess) {
+      hipLaunchKernelGGL(attn_split_combine_kernel, dim3((unsigned)(sp.n_split * (C::kBR / 8))), dim3(256), 0, st,
+                         sp.ws_o, sp.ws_lse, static_cast<uint16_t*>(o), lse, N, n_qtiles, sp);
+      err = hipGetLastError();
+    }
+    (void)hipFreeAsync(ws, st);
+  }
+  return err == hipSuccess ? DIT_ATTN_OK : DIT_ATTN_ELAUNCH;
 }
 
 template <class C>
@@ -159,7 +218,7 @@ int dit_attn_fwd_ex(const void* q, const void* k, const void* v, void* o, int B,
   if (dev_status != DIT_ATTN_OK) return dev_status;
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (dtype == DIT_ATTN_BF16) {
-    if (d == 128) return launch_pipe<CfgBf16D128>(q, k, v, o, lse, (int)bh, N, scale, st);
+    if (d == 128) return launch_pipe<CfgBf16D128>(q, k, v, o, lse, (int)bh, N, scale, st, cu_count());
     return launch_bf16<CfgBf16D64>(q, k, v, o, lse, (int)bh, N, scale, st);
   }
   return launch_fp8<CfgFp8D128>(q, k, v, o, lse, descale_qkv, (int)bh, N, scale, st);
