@@ -18,14 +18,22 @@
  * ---------------------------------------
  * Layout:    q, k, v, o are contiguous row-major [B][H][N][d] tensors, d
  *            innermost, in device memory. o is always bfloat16.
- * Ownership: the caller allocates, owns and frees every buffer. The library
- *            never allocates, frees or retains memory, never synchronises,
+ * Ownership: the caller allocates, owns and frees every buffer it passes.
+ *            One internal buffer exists: when a bf16 d = 128 call would leave
+ *            the GPU's last round of workgroups partly filled, those query
+ *            tiles are split along the keys and their fp32 partial rows go to
+ *            a stream-ordered scratch buffer (hipMallocAsync on `stream`,
+ *            released by hipFreeAsync on `stream` after the merge; at most
+ *            CUs x 256 rows x 129 floats, 33.8 MB on a 256-CU MI355X). If that
+ *            allocation fails the call runs unsplit, with the same result
+ *            semantics. The library retains no memory, never synchronises,
  *            and keeps no state beyond its loaded code objects and a
- *            per-device "is gfx950" flag.
+ *            per-device record (gfx950 or not, CU count).
  * Streams:   work is enqueued on `stream` (a hipStream_t; NULL = the null
  *            stream) and the call returns at once. The calls contain no host
- *            synchronisation, allocation or device-to-host read, so they may
- *            be captured in a HIP graph.
+ *            synchronisation or device-to-host read. Under HIP graph capture
+ *            the scratch buffer above becomes a stream-ordered allocation;
+ *            that case is not tested.
  * Errors:    every entry point returns DIT_ATTN_OK or a negative status, and
  *            launches nothing when it returns an error other than
  *            DIT_ATTN_ELAUNCH. Faults inside a kernel are not seen by the
