@@ -6,13 +6,13 @@
  *
  *     O[b,h] = softmax(Q[b,h] K[b,h]^T * scale) V[b,h]
  *
- * The pages this library follows name it only as the DiT's "dense" BF16
+ * The pages this library follows name it only as the DiT's dense BF16
  * attention, about 60% of DiT kernel time at 2048x2048 ("Speed Up Image
  * Generation with FLUX 3 Image Klein on NVIDIA Blackwell GPUs", "Key
  * takeaways"; Italian commentary, section "NVFP4, attention e caching"), and
  * report FP8 attention variants beside it (Japanese summary, third paragraph).
  * No mask is applied: every token attends to every token (the card's
- * glossary entry "transformer").
+ * glossary entry for the transformer).
  *
  * Conventions shared by every entry point
  * ---------------------------------------

@@ -12,8 +12,8 @@ reference-image tokens):
 
 Sources and readings
 --------------------
-* The pages name the operation only as the DiT's "dense" (also "standard",
-  "traditional") BF16 attention, which takes about 60% of DiT kernel time at
+* The pages name the operation only as the DiT's dense (also called standard
+  or traditional) BF16 attention, which takes about 60% of DiT kernel time at
   2048x2048 ("Speed Up Image Generation with FLUX 3 Image Klein on NVIDIA
   Blackwell GPUs", "Key takeaways"; Japanese summary, third paragraph;
   Italian commentary, section "NVFP4, attention e caching"). No formula is
