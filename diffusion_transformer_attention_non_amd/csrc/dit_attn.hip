@@ -100,22 +100,34 @@ int launch_bf16(const void* q, const void* k, const void* v, void* o, float* lse
 
 // One workgroup (256 query rows) runs per CU, so a grid of T tiles takes
 // ceil(T / n_cu) rounds and the last round holds rem = T mod n_cu tiles. Those
-// are split into `parts` key ranges (rem * parts <= n_cu, at least 4 key tiles
-// per range) that run side by side; a combine kernel merges them. The fp32
-// partial rows live in a stream-ordered allocation freed after the combine.
-// Returns 0 (no split) when the last round is full or more than half full,
-// or when the partial buffers cannot be had.
+// are split into `parts` contiguous key ranges that run side by side, and a
+// combine kernel merges them; the fp32 partial rows live in a stream-ordered
+// allocation freed after the merge. `parts` minimises the modelled time of
+// the last round, ceil(rem * parts / n_cu) * (1/parts + kPartOverhead / n_t)
+// in units of one full tile (each range pays about kPartOverhead key tiles of
+// prologue and epilogue), with at least 4 key tiles per range and at most
+// kMaxSplitRows partial rows. parts = 1 (no split) when nothing is gained.
+constexpr double kPartOverhead = 2.0;
+constexpr long long kMaxSplitRows = 1 << 18;     // 256 Ki rows x 129 floats = 135 MB
+
 int plan_split(int BH, int n_qtiles, int N, int n_cu, PipeSplit* sp) {
-  *sp = PipeSplit{BH * n_qtiles, 0, 1, nullptr, nullptr};
   const int tiles = BH * n_qtiles;
+  *sp = PipeSplit{tiles, 0, 1, nullptr, nullptr};
   const int rem = tiles % n_cu;
   const int n_t = (N + 63) / 64;
   if (rem == 0) return 0;
-  const int parts = std::min(n_cu / rem, n_t / 4);
-  if (parts < 2) return 0;
+  int best = 1;
+  double best_cost = 1.0;
+  const int max_parts = std::min<long long>(n_t / 4, kMaxSplitRows / (256LL * rem));
+  for (int parts = 2; parts <= max_parts; ++parts) {
+    const long long waves = ((long long)rem * parts + n_cu - 1) / n_cu;
+    const double cost = (double)waves * (1.0 / parts + kPartOverhead / n_t);
+    if (cost < best_cost * 0.98) { best_cost = cost; best = parts; }   // more parts only for a clear gain
+  }
+  if (best < 2) return 0;
   sp->n_full = tiles - rem;
   sp->n_split = rem;
-  sp->parts = parts;
+  sp->parts = best;
   return 1;
 }
 

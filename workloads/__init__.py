@@ -69,6 +69,13 @@ WORKLOADS = {
                              note="2048x2048-equivalent, inputs quantised to e4m3 per tensor, output bf16"),
     "i2i_2048": Workload("i2i_2048", 1, 24, 25088, 128, 512, 16384, n_ref=8192,
                          note="image-to-image-equivalent: 512 text + 128x128 target + 2x64x64 reference tokens"),
+    # One GPU's share of the 2048x2048-equivalent call under sequence
+    # parallelism over the heads: 24 heads over 4 (cfg 2 x ulysses 4 on 8 GPUs)
+    # or 8 sequence-parallel ranks.
+    "t2i_2048_h6": Workload("t2i_2048_h6", 1, 6, 16896, 128, 512, 16384,
+                            note="per-GPU share of t2i_2048 with 4-way head sharding"),
+    "t2i_2048_h3": Workload("t2i_2048_h3", 1, 3, 16896, 128, 512, 16384,
+                            note="per-GPU share of t2i_2048 with 8-way head sharding"),
 }
 
 
