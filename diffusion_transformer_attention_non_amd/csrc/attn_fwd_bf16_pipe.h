@@ -13,9 +13,11 @@
 // Rows are padded (K 272 bytes, V 320 bytes) so that every fragment read is
 // free of bank conflicts and addressed by one register plus an immediate; the
 // DMA writes 1 KB of consecutive LDS per instruction, and lanes that land on
-// padding fetch a harmless in-tile chunk. K lives in a ring of 3 tile slots and
-// V in a ring of 2: tile u is computed on while K tile u+2 and V tile u+1
-// stream in, and one s_waitcnt + barrier per 64 keys publishes them.
+// padding are pointed past the tile, so the range check zero-fills them
+// without a memory access. K lives in a ring of 4 tile slots and V in a ring
+// of 3: while tile u is computed on, K tile u+3 and V tile u+2 stream in (one
+// DMA instruction per MFMA step of phase Y), and one s_waitcnt + barrier per
+// 64 keys publishes the tiles issued an iteration earlier.
 //
 // Sub-iteration j (32 keys), two phases of 16 MFMAs each:
 //   X: O^T += V_{j-1}^T P_{j-1}^T, interleaved with the exponent arguments of
@@ -146,8 +148,10 @@ void attn_fwd_bf16_pipe_kernel(const uint16_t* __restrict__ Qg, const uint16_t* 
     const int s = 64 * (wave + 4 * m) + lane;
     const int kr = s / (KROW / 16), kc = s % (KROW / 16);
     const int vr = s / (VROW / 16), vc = s % (VROW / 16);
-    kdo[m] = kr * D * 2 + (kc < D / 8 ? kc * 16 : 0);
-    vdo[m] = vr * D * 2 + (vc < D / 8 ? vc * 16 : 0);
+    // padding slots get an offset past any tile (64 rows), so the range check
+    // zero-fills them without a memory access
+    kdo[m] = kc < D / 8 ? kr * D * 2 + kc * 16 : 64 * D * 2;
+    vdo[m] = vc < D / 8 ? vr * D * 2 + vc * 16 : 64 * D * 2;
   }
   // buffer descriptor of one 64-key tile: the range check zero-fills rows past N
   auto tile_rsrc = [&](const char* head, int t) __attribute__((always_inline)) {
