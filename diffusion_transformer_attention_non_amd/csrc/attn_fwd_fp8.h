@@ -5,8 +5,11 @@
 // e4m3 x e4m3 form. Per-tensor descales dq, dk fold into the logit
 // multiplier and dv into the epilogue. The probabilities, below 2^TAU
 // relative to the running maximum, are multiplied by 2^(8-TAU) (so at most
-// 256 < 448) and rounded to e4m3 (round-to-nearest-even) before the second
-// contraction; the row sum uses the unrounded fp32 values.
+// 256 < 448; the factor is added to the exponent argument, not multiplied)
+// and rounded to e4m3 (round-to-nearest-even) before the second
+// contraction; the row sum uses the unrounded fp32 values. The last, partly
+// filled round of workgroups is split along the keys like the bf16 kernel's
+// (PipeSplit, attn_split_combine_kernel).
 //
 // The two MFMA operands of one product must place the same k index in the
 // same (half-wave, byte) slot; any such placement gives the same sum. For
@@ -16,6 +19,7 @@
 // receives one d-column of an 8-key x 16-column block.
 #pragma once
 #include "attn_common.h"
+#include "attn_fwd_bf16_pipe.h"     // PipeSplit
 
 namespace ditattn {
 
@@ -37,7 +41,7 @@ struct Fp8Cfg {
 };
 
 constexpr float kTauFp8 = 4.0f;
-constexpr float kPScaleFp8 = 16.0f;     // 2^(8 - TAU)
+constexpr float kPScaleLog2Fp8 = 4.0f;   // P is scaled by 2^(8 - TAU) = 16
 
 // LDS serves 256 bytes (64 four-byte banks) per pass; with 128-byte rows two
 // rows share a pass, one in each half (row parity). Both swizzles below
@@ -65,7 +69,7 @@ __global__ __launch_bounds__(C::kThreads)
 void attn_fwd_fp8_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __restrict__ Kg,
                          const uint8_t* __restrict__ Vg, uint16_t* __restrict__ Og,
                          float* __restrict__ LSEg, const float* __restrict__ descale,
-                         int N, int n_qtiles, float scale_log2, float scale) {
+                         int N, int n_qtiles, float scale_log2, float scale, PipeSplit split) {
   constexpr int D = 128, QB = C::kQB, KB = C::kKB, KS = C::kKS, DB = C::kDB, KBLK = C::kKBLK;
   constexpr int CH = C::kChunks, TB = C::kTileBytes;
   extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -74,7 +78,20 @@ void attn_fwd_fp8_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __restri
   if (descale != nullptr) { dq = descale[0]; dk = descale[1]; dv = descale[2]; }
   const float c_log2 = scale_log2 * dq * dk;       // raw fp8 dot -> log2 units
 
-  const int tile = xcd_remap(blockIdx.x, gridDim.x);
+  const int n_kt = (N + KB - 1) / KB;
+  // query tile and key-tile range [kt0, kt1) of this workgroup
+  int tile, kt0 = 0, kt1 = n_kt, ws_index = -1;
+  if ((int)blockIdx.x < split.n_full) {
+    tile = xcd_remap(blockIdx.x, split.n_full);
+  } else {
+    const int sidx = xcd_remap(blockIdx.x - split.n_full, gridDim.x - split.n_full);
+    const int part = sidx / split.n_split;
+    const int ti = sidx - part * split.n_split;
+    tile = split.n_full + ti;
+    kt0 = part * n_kt / split.parts;
+    kt1 = (part + 1) * n_kt / split.parts;
+    ws_index = part * split.n_split + ti;
+  }
   const int bh = tile / n_qtiles;
   const int qt = tile - bh * n_qtiles;
   const size_t base = (size_t)bh * (size_t)N * D;
@@ -115,8 +132,6 @@ void attn_fwd_fp8_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __restri
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) { m_run[qb] = -INFINITY; l_run[qb] = 0.f; }
 
-  const int n_kt = (N + KB - 1) / KB;
-
   i32x4_t stK[C::kLoadsPerThread], stV[C::kLoadsPerThread];
   auto load_tile = [&](int kt) {
 #pragma unroll
@@ -145,7 +160,7 @@ void attn_fwd_fp8_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __restri
     }
   };
 
-  load_tile(0);
+  load_tile(kt0);
   store_tile(0);
   __syncthreads();
 
@@ -156,9 +171,9 @@ void attn_fwd_fp8_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __restri
   const int tr_chunk = g & 1;                                          // chunk within a 32-wide d block
   const int tr_off = (gi & 1) * 8;
 
-  for (int kt = 0; kt < n_kt; ++kt) {
-    const int buf = kt & 1;
-    const bool has_next = kt + 1 < n_kt;
+  for (int kt = kt0; kt < kt1; ++kt) {
+    const int buf = (kt - kt0) & 1;
+    const bool has_next = kt + 1 < kt1;
     if (has_next) load_tile(kt + 1);
     const char* kbuf = smem + buf * 2 * TB;
     const char* vbuf = kbuf + TB;
@@ -227,7 +242,7 @@ void attn_fwd_fp8_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __restri
     i32x8_t pb[KBLK / 2][QB];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      const float mc = m_run[qb] * c_log2;
+      const float mc = m_run[qb] * c_log2 - kPScaleLog2Fp8;   // p scaled by 16
       float ls = 0.f;
 #pragma unroll
       for (int kp = 0; kp < KBLK / 2; ++kp) {
@@ -241,7 +256,7 @@ void attn_fwd_fp8_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __restri
             p[e] = fast_exp2(fmaf(s[kb][qb][(t & 3) * 4 + e], c_log2, -mc));
             ls += p[e];
           }
-          w[t] = (int)pack_e4m3x4(p[0] * kPScaleFp8, p[1] * kPScaleFp8, p[2] * kPScaleFp8, p[3] * kPScaleFp8);
+          w[t] = (int)pack_e4m3x4(p[0], p[1], p[2], p[3]);
         }
         pb[kp][qb] = w;
       }
@@ -272,10 +287,32 @@ void attn_fwd_fp8_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __restri
     __syncthreads();
   }
 
+  // l_run sums 16 p, and so does acc: their ratio needs no further scaling
+  if (ws_index >= 0) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const float l_tot = pair_sum(l_run[qb]);
+      const float mul = dv / l_tot;
+      const int r = wave * QB * 32 + qb * 32 + l32;
+      float* orow = split.ws_o + ((size_t)ws_index * C::kBR + r) * D;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int d0 = db * 32 + i * 8 + hh * 4;
+          f32x4_t w = {acc[qb][db][i * 4 + 0] * mul, acc[qb][db][i * 4 + 1] * mul, acc[qb][db][i * 4 + 2] * mul,
+                       acc[qb][db][i * 4 + 3] * mul};
+          *(f32x4_t*)(orow + d0) = w;
+        }
+      if (hh == 0)
+        split.ws_lse[(size_t)ws_index * C::kBR + r] = m_run[qb] * c_log2 + __log2f(l_tot) - kPScaleLog2Fp8;
+    }
+    return;
+  }
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const float l_tot = pair_sum(l_run[qb]);
-    const float mul = dv / (kPScaleFp8 * l_tot);
+    const float mul = dv / l_tot;
     const int row = q0 + qb * 32 + l32;
     if (row < N) {
       uint16_t* orow = Og + base + (size_t)row * D;
@@ -290,7 +327,7 @@ void attn_fwd_fp8_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __restri
           *(uint2*)(orow + d0) = w;
         }
       if (LSEg != nullptr && hh == 0)
-        LSEg[(size_t)bh * N + row] = m_run[qb] * scale * dq * dk + logf(l_tot);
+        LSEg[(size_t)bh * N + row] = (m_run[qb] * c_log2 + __log2f(l_tot) - kPScaleLog2Fp8) * 0.6931471805599453f;
     }
   }
 }

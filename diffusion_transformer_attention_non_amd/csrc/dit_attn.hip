@@ -110,11 +110,11 @@ int launch_bf16(const void* q, const void* k, const void* v, void* o, float* lse
 constexpr double kPartOverhead = 2.0;
 constexpr long long kMaxSplitRows = 1 << 18;     // 256 Ki rows x 129 floats = 135 MB
 
-int plan_split(int BH, int n_qtiles, int N, int n_cu, PipeSplit* sp) {
+int plan_split(int BH, int n_qtiles, int N, int key_tile, int n_cu, PipeSplit* sp) {
   const int tiles = BH * n_qtiles;
   *sp = PipeSplit{tiles, 0, 1, nullptr, nullptr};
   const int rem = tiles % n_cu;
-  const int n_t = (N + 63) / 64;
+  const int n_t = (N + key_tile - 1) / key_tile;
   if (rem == 0) return 0;
   int best = 1;
   double best_cost = 1.0;
@@ -140,7 +140,7 @@ int launch_pipe(const void* q, const void* k, const void* v, void* o, float* lse
   const float scale_log2 = scale * 1.4426950408889634f;
   PipeSplit sp;
   void* ws = nullptr;
-  if (plan_split(BH, n_qtiles, N, n_cu, &sp)) {
+  if (plan_split(BH, n_qtiles, N, 64, n_cu, &sp)) {
     const size_t units = (size_t)sp.n_split * sp.parts * C::kBR;
     if (hipMallocAsync(&ws, units * (C::kD + 1) * sizeof(float), st) == hipSuccess && ws != nullptr) {
       sp.ws_o = static_cast<float*>(ws);
@@ -170,16 +170,40 @@ int launch_pipe(const void* q, const void* k, const void* v, void* o, float* lse
 
 template <class C>
 int launch_fp8(const void* q, const void* k, const void* v, void* o, float* lse, const float* descale,
-               int BH, int N, float scale, hipStream_t st) {
+               int BH, int N, float scale, hipStream_t st, int n_cu) {
   const int n_qtiles = (N + C::kBR - 1) / C::kBR;
-  const long long grid = (long long)n_qtiles * BH;
-  if (grid > 0x7fffffffLL) return DIT_ATTN_EINVAL;
+  const long long tiles = (long long)n_qtiles * BH;
+  if (tiles > 0x7fffffffLL / 8) return DIT_ATTN_EINVAL;
+  static_assert(C::kBR == PipeCfg::kBR && C::kD == PipeCfg::kD, "the merge kernel assumes 256 x 128 tiles");
   const float scale_log2 = scale * 1.4426950408889634f;
+  PipeSplit sp;
+  void* ws = nullptr;
+  if (plan_split(BH, n_qtiles, N, C::kKB, n_cu, &sp)) {
+    const size_t units = (size_t)sp.n_split * sp.parts * C::kBR;
+    if (hipMallocAsync(&ws, units * (C::kD + 1) * sizeof(float), st) == hipSuccess && ws != nullptr) {
+      sp.ws_o = static_cast<float*>(ws);
+      sp.ws_lse = sp.ws_o + units * C::kD;
+    } else {
+      (void)hipGetLastError();
+      ws = nullptr;
+      sp = PipeSplit{(int)tiles, 0, 1, nullptr, nullptr};
+    }
+  }
+  const long long grid = (long long)sp.n_full + (long long)sp.n_split * sp.parts;
   hipLaunchKernelGGL(attn_fwd_fp8_kernel<C>, dim3((unsigned)grid), dim3(C::kThreads), C::kLdsBytes, st,
                      static_cast<const uint8_t*>(q), static_cast<const uint8_t*>(k),
                      static_cast<const uint8_t*>(v), static_cast<uint16_t*>(o), lse, descale, N, n_qtiles,
-                     scale_log2, scale);
-  return hipGetLastError() == hipSuccess ? DIT_ATTN_OK : DIT_ATTN_ELAUNCH;
+                     scale_log2, scale, sp);
+  hipError_t err = hipGetLastError();
+  if (ws != nullptr) {
+    if (err == hipSuccess) {
+      hipLaunchKernelGGL(attn_split_combine_kernel, dim3((unsigned)(sp.n_split * (C::kBR / 8))), dim3(256), 0, st,
+                         sp.ws_o, sp.ws_lse, static_cast<uint16_t*>(o), lse, N, n_qtiles, sp);
+      err = hipGetLastError();
+    }
+    (void)hipFreeAsync(ws, st);
+  }
+  return err == hipSuccess ? DIT_ATTN_OK : DIT_ATTN_ELAUNCH;
 }
 
 }  // namespace
@@ -233,7 +257,7 @@ int dit_attn_fwd_ex(const void* q, const void* k, const void* v, void* o, int B,
     if (d == 128) return launch_pipe<CfgBf16D128>(q, k, v, o, lse, (int)bh, N, scale, st, cu_count());
     return launch_bf16<CfgBf16D64>(q, k, v, o, lse, (int)bh, N, scale, st);
   }
-  return launch_fp8<CfgFp8D128>(q, k, v, o, lse, descale_qkv, (int)bh, N, scale, st);
+  return launch_fp8<CfgFp8D128>(q, k, v, o, lse, descale_qkv, (int)bh, N, scale, st, cu_count());
 }
 
 int dit_attn_fwd(const void* q, const void* k, const void* v, void* o, int B, int H, int N, int d, float scale,
