@@ -1,0 +1,428 @@
+// fp8-e4m3 attention forward for gfx950, d = 128, bf16 out: 64 query rows per
+// wave, software-pipelined, K/V tiles moved by LDS DMA.
+//
+// The structure follows attn_fwd_bf16_pipe.h (one wave per SIMD, 4 waves and
+// 256 rows per workgroup, K in a ring of 4 LDS slots and V in a ring of 3,
+// filled two tiles ahead by buffer_load ... lds, one barrier per tile, the
+// running maximum moved only on a rare path, key-range split of the last
+// round). What differs for e4m3:
+// * both products run on the 32x32x64 f8f6f4 MFMA in its e4m3 x e4m3 form, so
+//   a sub-tile is 64 keys (the k extent of the PV product) and an LDS tile 128;
+// * K rows are 128 bytes padded to 144 (conflict-free ds_read_b128, additive
+//   addresses); V rows keep 128 bytes with the transpose-read-aware XOR
+//   swizzle of attn_fwd_fp8.h, which the DMA applies by choosing each lane's
+//   source chunk; V^T fragments come from ds_read_b64_tr_b8 and P^T is packed
+//   from the S^T accumulators in the matching key order;
+// * probabilities are scaled by 8 before the e4m3 cast (the factor is added
+//   to the exponent argument), and the row sums use the unrounded fp32
+//   values. The e4m3 cast saturates above 448, i.e. for p > 56 relative to
+//   the running maximum; a row sum above 448 in some lane (which any such p
+//   implies, and which 32 probabilities of at most 1 cannot reach) sends the
+//   sub-tile down the rare path, which recomputes its logits from K in LDS,
+//   takes their exact maximum and rescales;
+// * per-tensor descales dq, dk fold into the logit multiplier and dv into the
+//   epilogue.
+// Sub-iteration j (64 keys), two phases of 8 MFMAs each:
+//   X: O^T += V_{j-1}^T P_{j-1}^T, with the softmax of S_j's first query block;
+//      the K_{j+1} fragment reads are issued first.
+//   Y: S_{j+1} = K_{j+1} Q^T, with the softmax of S_j's second query block, the
+//      V_j fragment reads and the tile DMA.
+#pragma once
+#include "attn_common.h"
+#include "attn_fwd_bf16_pipe.h"   // dma_b128, flag_t, PipeSplit
+#include "attn_fwd_fp8.h"         // swz8_v, pack_e4m3x4
+
+namespace ditattn {
+
+struct Fp8PipeCfg {
+  static constexpr int kD = 128, kNW = 4, kThreads = 256, kBR = 256;
+  static constexpr int kKRow = 144;                        // K row pitch in LDS: 128 bytes + 16 padding
+  static constexpr int kTileKeys = 128;                    // keys per LDS tile (two 64-key sub-tiles)
+  static constexpr int kKB = kTileKeys;                    // key-tile size for the split planner
+  static constexpr int kKTile = kTileKeys * kKRow;         // 18432
+  static constexpr int kVTile = kTileKeys * 128;           // 16384
+  static constexpr int kDmaPerWave = 5;                    // 20 x 1 KB instructions per tile and tensor
+  static constexpr int kSlot = kNW * kDmaPerWave * 1024;   // 20480
+  static constexpr int kKSlots = 4, kVSlots = 3;
+  static constexpr int kVBase = kKSlots * kSlot;
+  static constexpr int kLdsBytes = kVBase + kVSlots * kSlot;   // 143360
+  static_assert(kKTile <= kSlot && kVTile <= kSlot, "tile fits its slot");
+};
+
+constexpr float kFp8PipeSumLimit = 448.0f;     // largest e4m3 value
+constexpr float kFp8PipePLog2 = 3.0f;          // P is scaled by 2^3 before the cast
+
+#define DIT_FENCE() __builtin_amdgcn_sched_barrier(0)
+
+template <class C>
+__global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void attn_fwd_fp8_pipe_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __restrict__ Kg,
+                              const uint8_t* __restrict__ Vg, uint16_t* __restrict__ Og,
+                              float* __restrict__ LSEg, const float* __restrict__ descale,
+                              int N, int n_qtiles, float scale_log2, float scale, PipeSplit split) {
+  constexpr int D = C::kD, KROW = C::kKRow;
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+
+  float dq = 1.f, dk = 1.f, dv = 1.f;
+  if (descale != nullptr) { dq = descale[0]; dk = descale[1]; dv = descale[2]; }
+  const float c_log2 = scale_log2 * dq * dk;          // raw fp8 dot -> log2 units
+
+  const int n_t = (N + C::kTileKeys - 1) / C::kTileKeys;
+  int tile, u0 = 0, u1 = n_t, ws_index = -1;
+  if ((int)blockIdx.x < split.n_full) {
+    tile = xcd_remap(blockIdx.x, split.n_full);
+  } else {
+    const int sidx = xcd_remap(blockIdx.x - split.n_full, gridDim.x - split.n_full);
+    const int part = sidx / split.n_split;
+    const int ti = sidx - part * split.n_split;
+    tile = split.n_full + ti;
+    u0 = part * n_t / split.parts;
+    u1 = (part + 1) * n_t / split.parts;
+    ws_index = part * split.n_split + ti;
+  }
+  const int bh = tile / n_qtiles;
+  const int qt = tile - bh * n_qtiles;
+  const size_t base = (size_t)bh * (size_t)N * D;
+  const char* Kh = reinterpret_cast<const char*>(Kg + base);
+  const char* Vh = reinterpret_cast<const char*>(Vg + base);
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int l32 = lane & 31, hh = lane >> 5;
+  const int q0 = qt * C::kBR + wave * 64;
+
+  // Q^T fragments: query q0 + qb*32 + l32, d = ks*64 + hh*32 .. +31
+  i32x8_t qf[2][2];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const int row = q0 + qb * 32 + l32;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      i32x4_t a = {0, 0, 0, 0}, b = {0, 0, 0, 0};
+      if (row < N) {
+        const uint8_t* p = Qg + base + (size_t)row * D + ks * 64 + hh * 32;
+        a = *(const i32x4_t*)p;
+        b = *(const i32x4_t*)(p + 16);
+      }
+      qf[qb][ks] = i32x8_t{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    }
+  }
+
+  // ---- DMA lane offsets: instruction i writes LDS bytes [1024 i, 1024 i + 1024)
+  // of a slot; lane L covers 16-byte slot s = 64 i + L
+  int kdo[C::kDmaPerWave], vdo[C::kDmaPerWave];
+#pragma unroll
+  for (int m = 0; m < C::kDmaPerWave; ++m) {
+    const int s = 64 * (wave + 4 * m) + lane;
+    const int kr = s / (KROW / 16), kc = s % (KROW / 16);
+    kdo[m] = (kc < 8 && kr < C::kTileKeys) ? kr * D + kc * 16 : C::kTileKeys * D;   // past the tile: zeros
+    const int vr = s >> 3, vs = s & 7;
+    const int vc = vs ^ ((((vr >> 1) & 1) << 1) | (((vr >> 3) & 1) << 2));    // inverse of swz8_v
+    vdo[m] = vr < C::kTileKeys ? vr * D + vc * 16 : C::kTileKeys * D;
+  }
+  auto tile_rsrc = [&](const char* head, int t) __attribute__((always_inline)) {
+    const int rows = min(C::kTileKeys, N - t * C::kTileKeys);
+    const unsigned long long a = (unsigned long long)(head + (size_t)t * C::kTileKeys * D);
+    i32x4_t rs;
+    rs[0] = __builtin_amdgcn_readfirstlane((int)(unsigned)a);
+    rs[1] = __builtin_amdgcn_readfirstlane((int)((a >> 32) & 0xffffu));
+    rs[2] = __builtin_amdgcn_readfirstlane(rows * D);
+    rs[3] = 0x00020000;
+    return rs;
+  };
+  auto dma_one = [&](const i32x4_t& rs, const char* slot, const int (&off)[C::kDmaPerWave], int m)
+      __attribute__((always_inline)) {
+    const int i = wave + 4 * m;
+    dma_b128(rs, off[m], __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)DIT_LDS(const char, slot) + i * 1024));
+  };
+  auto dma_tile = [&](const char* head, int t, const char* slot, const int (&off)[C::kDmaPerWave])
+      __attribute__((always_inline)) {
+    const i32x4_t rs = tile_rsrc(head, t);
+#pragma unroll
+    for (int m = 0; m < C::kDmaPerWave; ++m) dma_one(rs, slot, off, m);
+  };
+  auto kslot = [&](int t) { return smem + __builtin_amdgcn_readfirstlane((t % C::kKSlots) * C::kSlot); };
+  auto vslot = [&](int t) {
+    return smem + __builtin_amdgcn_readfirstlane(C::kVBase + (t % C::kVSlots) * C::kSlot);
+  };
+
+  // ---- fragment reads
+  const int k_rd = l32 * KROW + hh * 32;
+  i32x8_t kf[2][2];                                     // [key block][d step]
+  auto read_kfrags = [&](int j) {
+    const char* kb = kslot(j >> 1) + (j & 1) * 64 * KROW + k_rd;
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const i32x4_t a0 = *(const i32x4_t*)(kb + b * 32 * KROW + ks * 64);
+        const i32x4_t a1 = *(const i32x4_t*)(kb + b * 32 * KROW + ks * 64 + 16);
+        kf[b][ks] = i32x8_t{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+      }
+  };
+  // V^T gather (the key order of the P^T packing): lane pair gi>>1 addresses key
+  // slot tr_e of an 8-key read; the XOR of the V swizzle depends on key bits
+  // 1 and 3, which come from tr_key alone
+  const int g = lane >> 4, gi = lane & 15;
+  const int tr_e = gi >> 1;
+  const int tr_key = (tr_e >> 2) * 8 + (g >> 1) * 4 + (tr_e & 3);
+  const int tr_gk = (((tr_key >> 1) & 1) << 1) | (((tr_key >> 3) & 1) << 2);
+  int v_rd[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db) v_rd[db] = tr_key * 128 + (((2 * db) ^ tr_gk) + (g & 1)) * 16 + (gi & 1) * 8;
+  i32x8_t vf[4];                                        // [d block]
+  auto read_vfrags = [&](int j, int half) {             // half 0: d blocks 0, 1; half 1: 2, 3
+    const char* vb = vslot(j >> 1) + (j & 1) * 64 * 128;
+#pragma unroll
+    for (int db = half * 2; db < half * 2 + 2; ++db) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const i32x2_t t = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+            DIT_LDS(i32x2_t, (vb + ((u >> 1) * 32 + (u & 1) * 16) * 128 + v_rd[db])));
+        vf[db][2 * u] = t[0];
+        vf[db][2 * u + 1] = t[1];
+      }
+    }
+  };
+  // keys of sub-tile j past N do not exist
+  auto mask_keys = [&](int j, f32x16_t (&s)[2]) {
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = j * 64 + b * 32 + (r >> 2) * 8 + hh * 4 + (r & 3);
+        s[b][r] = key < N ? s[b][r] : -INFINITY;
+      }
+  };
+  auto s_chains = [&](int qb, f32x16_t (&s)[2]) {
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[b][r] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+        s[b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kf[b][ks], qf[qb][ks], s[b], 0, 0, 0, 0, 0, 0);
+    }
+  };
+  auto row_max = [&](const f32x16_t (&s)[2]) {
+    float mx = fmaxf(s[0][0], s[1][0]);
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(s[0][r], s[1][r]));
+    return pair_max(mx) * c_log2;                     // c_log2 > 0
+  };
+  // one step of the softmax of one query block: 4 logits -> 8 p, one e4m3 word
+  auto soft_step = [&](const f32x16_t (&s)[2], int w, float nm, i32x8_t& pout, float& ls) {
+    const int b = w >> 2, r0 = (w & 3) * 4;
+    float p[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      p[e] = fast_exp2(fmaf(s[b][r0 + e], c_log2, nm));
+      ls += p[e];
+    }
+    pout[w] = (int)pack_e4m3x4(p[0], p[1], p[2], p[3]);
+  };
+
+  f32x16_t acc[2][4];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[qb][db][r] = 0.f;
+  float mc[2];                        // running row maxima of the scaled logits, log2 units
+  float l_run[2] = {0.f, 0.f};        // sums of 8 p
+  f32x16_t s0[2];                     // raw logits of the current sub-tile, query block 0
+  f32x16_t s1A[2], s1B[2];            // query block 1, alternating between sub-tiles
+  i32x8_t pA[2], pB[2];               // P^T of two consecutive sub-tiles [query block]
+
+  // ---- prologue: K tiles u0..u0+2, V tiles u0, u0+1; the first sub-tile's logits
+  dma_tile(Kh, u0, kslot(u0), kdo);
+  if (u0 + 1 < u1) dma_tile(Kh, u0 + 1, kslot(u0 + 1), kdo);
+  if (u0 + 2 < u1) dma_tile(Kh, u0 + 2, kslot(u0 + 2), kdo);
+  dma_tile(Vh, u0, vslot(u0), vdo);
+  if (u0 + 1 < u1) dma_tile(Vh, u0 + 1, vslot(u0 + 1), vdo);
+  __builtin_amdgcn_s_waitcnt(0x0F70);      // vmcnt(0)
+  __syncthreads();
+  read_kfrags(2 * u0);
+  s_chains(0, s0);
+  s_chains(1, s1A);
+  if (64 * (2 * u0 + 1) > N) { mask_keys(2 * u0, s0); mask_keys(2 * u0, s1A); }
+  mc[0] = row_max(s0);
+  mc[1] = row_max(s1A);
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) pA[qb] = i32x8_t{};
+#pragma unroll
+  for (int db = 0; db < 4; ++db) vf[db] = i32x8_t{};
+
+  // One sub-iteration: consumes P_{j-1} (pin) and S_j (s0, s1in); produces
+  // P_j (pout) and S_{j+1} (s0, s1out).
+  auto sub = [&](int j, i32x8_t (&pin)[2], i32x8_t (&pout)[2], f32x16_t (&s1in)[2], f32x16_t (&s1out)[2],
+                 auto mask_c, auto&& dma) __attribute__((always_inline)) {
+    constexpr bool MASK = decltype(mask_c)::value;
+    float ls0 = 0.f, ls1 = 0.f;
+    // ================= phase X
+    read_kfrags(j + 1);
+    DIT_FENCE();
+    {
+      const float nm0 = kFp8PipePLog2 - mc[0];
+#pragma unroll
+      for (int st = 0; st < 8; ++st) {
+        const int db = st >> 1, qb = st & 1;
+        acc[qb][db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vf[db], pin[qb], acc[qb][db], 0, 0, 0, 0, 0, 0);
+        soft_step(s0, st, nm0, pout[0], ls0);
+        DIT_FENCE();
+      }
+    }
+    // ================= phase Y
+    {
+      f32x16_t n0[2];
+      const float nm1 = kFp8PipePLog2 - mc[1];
+#pragma unroll
+      for (int st = 0; st < 8; ++st) {
+        const int b = st >> 2, qb = (st >> 1) & 1, ks = st & 1;
+        f32x16_t& dst = qb == 0 ? n0[b] : s1out[b];
+        if (ks == 0) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) dst[r] = 0.f;
+        }
+        dst = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kf[b][ks], qf[qb][ks], dst, 0, 0, 0, 0, 0, 0);
+        // the V_j fragment reads go behind the first MFMAs (the K fragments
+        // were read a phase earlier); 8 at a time, lgkmcnt counts at most 15
+        if (st < 2) {
+          DIT_FENCE();
+          read_vfrags(j, st);
+          DIT_FENCE();
+        }
+        soft_step(s1in, st, nm1, pout[1], ls1);
+        if (st >= 4) dma(st - 4);
+        DIT_FENCE();
+      }
+      if constexpr (MASK) {
+        if (64 * (j + 2) > N) { mask_keys(j + 1, n0); mask_keys(j + 1, s1out); }
+      }
+      s0[0] = n0[0];
+      s0[1] = n0[1];
+    }
+    // The packed P must exist here: without this the compiler sinks the e4m3
+    // conversions past the rare-path branch, out of the MFMA phases.
+    asm volatile("" ::"v"(pout[0]), "v"(pout[1]));
+    // ---- rare path: some lane's p reached the e4m3 range limit
+    const bool bad = !(ls0 <= kFp8PipeSumLimit) || !(ls1 <= kFp8PipeSumLimit);
+    if (__builtin_amdgcn_ballot_w64(bad) != 0) {
+      read_kfrags(j);                      // K tile j/2 is still in its slot
+      ls0 = 0.f;
+      ls1 = 0.f;
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        f32x16_t s[2];
+        s_chains(qb, s);
+        if constexpr (MASK) {
+          if (64 * (j + 1) > N) mask_keys(j, s);
+        }
+        const float m_new = fmaxf(mc[qb], row_max(s));
+        const float alpha = fast_exp2(mc[qb] - m_new);
+        l_run[qb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[qb][db][r] *= alpha;
+        mc[qb] = m_new;
+        const float nm = kFp8PipePLog2 - m_new;
+#pragma unroll
+        for (int w = 0; w < 8; ++w) soft_step(s, w, nm, pout[qb], qb == 0 ? ls0 : ls1);
+      }
+    }
+    l_run[0] += ls0;
+    l_run[1] += ls1;
+  };
+
+  // One 128-key tile u: streams in K tile u+3 (first sub-iteration) and V tile
+  // u+2 (second), one DMA instruction per phase-Y step, then waits for the
+  // tiles issued one iteration earlier before the barrier that publishes them.
+  auto iteration = [&](int u, auto tail_c) __attribute__((always_inline)) {
+    constexpr bool TAIL = decltype(tail_c)::value;
+    const bool k_next = !TAIL || u + 3 < u1, v_next = !TAIL || u + 2 < u1;
+    const i32x4_t rk = tile_rsrc(Kh, u + 3), rv = tile_rsrc(Vh, u + 2);
+    const char* sk = kslot(u + 3);
+    const char* sv = vslot(u + 2);
+    DIT_FENCE();
+    static_assert(C::kDmaPerWave == 5, "DMA hook spreads 5 instructions over 4 steps");
+    sub(2 * u, pA, pB, s1A, s1B, tail_c, [&](int st) __attribute__((always_inline)) {
+      if (k_next) {
+        dma_one(rk, sk, kdo, st);
+        if (st == 0) dma_one(rk, sk, kdo, 4);
+      }
+    });
+    sub(2 * u + 1, pB, pA, s1B, s1A, tail_c, [&](int st) __attribute__((always_inline)) {
+      if (v_next) {
+        dma_one(rv, sv, vdo, st);
+        if (st == 0) dma_one(rv, sv, vdo, 4);
+      }
+    });
+    DIT_FENCE();
+    if (TAIL)
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    else
+      __builtin_amdgcn_s_waitcnt(0x0F7A);  // vmcnt(10): this iteration's 10 DMAs may stay in flight
+    __syncthreads();
+    DIT_FENCE();
+  };
+  int u = u0;
+  for (; u + 3 < u1; ++u) iteration(u, flag_t<false>{});
+  for (; u < u1; ++u) iteration(u, flag_t<true>{});
+
+  // ---- P V of the last sub-tile (its V fragments were read in the last phase Y)
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+      acc[qb][db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vf[db], pA[qb], acc[qb][db], 0, 0, 0, 0, 0, 0);
+
+  // l_run sums 8 p, and so does acc: their ratio needs no further scaling
+  if (ws_index >= 0) {
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      const float l_tot = pair_sum(l_run[qb]);
+      const float mul = dv / l_tot;
+      const int r = wave * 64 + qb * 32 + l32;
+      float* orow = split.ws_o + ((size_t)ws_index * C::kBR + r) * D;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int d0 = db * 32 + i * 8 + hh * 4;
+          f32x4_t w = {acc[qb][db][i * 4 + 0] * mul, acc[qb][db][i * 4 + 1] * mul, acc[qb][db][i * 4 + 2] * mul,
+                       acc[qb][db][i * 4 + 3] * mul};
+          *(f32x4_t*)(orow + d0) = w;
+        }
+      if (hh == 0) split.ws_lse[(size_t)ws_index * C::kBR + r] = mc[qb] + __log2f(l_tot) - kFp8PipePLog2;
+    }
+    return;
+  }
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const float l_tot = pair_sum(l_run[qb]);
+    const float mul = dv / l_tot;
+    const int row = q0 + qb * 32 + l32;
+    if (row < N) {
+      uint16_t* orow = Og + base + (size_t)row * D;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int d0 = db * 32 + i * 8 + hh * 4;
+          uint2 w;
+          w.x = pack_bf16x2(acc[qb][db][i * 4 + 0] * mul, acc[qb][db][i * 4 + 1] * mul);
+          w.y = pack_bf16x2(acc[qb][db][i * 4 + 2] * mul, acc[qb][db][i * 4 + 3] * mul);
+          *(uint2*)(orow + d0) = w;
+        }
+      if (LSEg != nullptr && hh == 0)
+        LSEg[(size_t)bh * N + row] = (mc[qb] + __log2f(l_tot) - kFp8PipePLog2) * 0.6931471805599453f;
+    }
+  }
+}
+
+#undef DIT_FENCE
+
+}  // namespace ditattn

@@ -12,6 +12,7 @@
 #include "attn_fwd_bf16.h"
 #include "attn_fwd_bf16_pipe.h"
 #include "attn_fwd_fp8.h"
+#include "attn_fwd_fp8_pipe.h"
 #include "quant_e4m3.h"
 
 using namespace ditattn;
@@ -29,7 +30,7 @@ int g_num_cu[kMaxDevices];
 // BR = NW * QB * 32 rows per workgroup.
 using CfgBf16D128 = PipeCfg;
 using CfgBf16D64 = Bf16Cfg<64, 1, 8, 64, 2>;
-using CfgFp8D128 = Fp8Cfg<1, 8, 128>;
+using CfgFp8D128 = Fp8PipeCfg;
 
 template <class C>
 hipError_t allow_lds_bf16() {
@@ -43,7 +44,7 @@ hipError_t allow_lds_pipe() {
 }
 template <class C>
 hipError_t allow_lds_fp8() {
-  return hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_fwd_fp8_kernel<C>),
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_fwd_fp8_pipe_kernel<C>),
                              hipFuncAttributeMaxDynamicSharedMemorySize, C::kLdsBytes);
 }
 
@@ -190,7 +191,7 @@ int launch_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
     }
   }
   const long long grid = (long long)sp.n_full + (long long)sp.n_split * sp.parts;
-  hipLaunchKernelGGL(attn_fwd_fp8_kernel<C>, dim3((unsigned)grid), dim3(C::kThreads), C::kLdsBytes, st,
+  hipLaunchKernelGGL(attn_fwd_fp8_pipe_kernel<C>, dim3((unsigned)grid), dim3(C::kThreads), C::kLdsBytes, st,
                      static_cast<const uint8_t*>(q), static_cast<const uint8_t*>(k),
                      static_cast<const uint8_t*>(v), static_cast<uint16_t*>(o), lse, descale, N, n_qtiles,
                      scale_log2, scale, sp);
