@@ -74,7 +74,8 @@ constexpr float kPipeSumLimit = 256.0f;    // 2^8
 struct PipeSplit {
   int n_full, n_split, parts;
   float* ws_o;      // [n_split * parts][256][128]
-  float* ws_lse;    // [n_split * parts][256], log2 units
+  float* ws_lse;    // [n_split * parts][256], log2 units: the merge weights of O
+  float* ws_lse_out;  // NULL, or [n_split * parts][256]: a different log2 sum for the LSE output
 };
 
 template <bool B>
@@ -520,6 +521,14 @@ __global__ __launch_bounds__(256) void attn_split_combine_kernel(const float* __
   for (int p = 0; p < split.parts; ++p) mx = fmaxf(mx, ws_lse[(size_t)(p * split.n_split + ti) * BR + r]);
   float wsum = 0.f;
   f32x4_t o = {0.f, 0.f, 0.f, 0.f};
+  float lse_mx = mx, lse_sum = 0.f;    // the LSE output's own sums when ws_lse_out is given
+  if (LSEg != nullptr && split.ws_lse_out != nullptr && c == 0) {
+    lse_mx = -INFINITY;
+    for (int p = 0; p < split.parts; ++p)
+      lse_mx = fmaxf(lse_mx, split.ws_lse_out[(size_t)(p * split.n_split + ti) * BR + r]);
+    for (int p = 0; p < split.parts; ++p)
+      lse_sum += fast_exp2(split.ws_lse_out[(size_t)(p * split.n_split + ti) * BR + r] - lse_mx);
+  }
   for (int p = 0; p < split.parts; ++p) {
     const size_t idx = (size_t)(p * split.n_split + ti) * BR + r;
     const float w = fast_exp2(ws_lse[idx] - mx);
@@ -532,7 +541,9 @@ __global__ __launch_bounds__(256) void attn_split_combine_kernel(const float* __
   out.x = pack_bf16x2(o[0] * inv, o[1] * inv);
   out.y = pack_bf16x2(o[2] * inv, o[3] * inv);
   *(uint2*)(Og + ((size_t)bh * N + row) * D + c) = out;
-  if (LSEg != nullptr && c == 0) LSEg[(size_t)bh * N + row] = (mx + __log2f(wsum)) * 0.6931471805599453f;
+  if (LSEg != nullptr && c == 0)
+    LSEg[(size_t)bh * N + row] =
+        (split.ws_lse_out != nullptr ? lse_mx + __log2f(lse_sum) : mx + __log2f(wsum)) * 0.6931471805599453f;
 }
 
 }  // namespace ditattn

@@ -25,8 +25,9 @@
 // Sub-iteration j (64 keys), two phases of 8 MFMAs each:
 //   X: O^T += V_{j-1}^T P_{j-1}^T, with the softmax of S_j's first query block;
 //      the K_{j+1} fragment reads are issued first.
-//   Y: S_{j+1} = K_{j+1} Q^T, with the softmax of S_j's second query block, the
-//      V_j fragment reads and the tile DMA.
+//   Y: S_{j+1} = K_{j+1} Q^T, with the softmax of S_j's second query block (each
+//      block of S_j is overwritten once consumed), the V_j fragment reads and
+//      the tile DMA.
 #pragma once
 #include "attn_common.h"
 #include "attn_fwd_bf16_pipe.h"   // dma_b128, flag_t, PipeSplit
@@ -54,7 +55,22 @@ constexpr float kFp8PipePLog2 = 3.0f;          // P is scaled by 2^3 before the 
 
 #define DIT_FENCE() __builtin_amdgcn_sched_barrier(0)
 
-template <class C>
+// O^T += V^T P^T with the accumulator held in AGPRs. The builtin form would keep
+// it in VGPRs, where its 128 registers per lane push the logits out to AGPR
+// copies. The compiler does not model this instruction's latency: the
+// accumulator's AGPRs are read by the VALU only after pv_drain() or after a
+// full phase of other work, and its VGPR sources are not rewritten for a
+// whole sub-iteration after issue.
+__device__ __forceinline__ void pv_mfma(f32x16_t& acc, const i32x8_t& v, const i32x8_t& p) {
+  asm("v_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, %0" : "+a"(acc) : "v"(v), "v"(p));
+}
+// 32 wait states: more than a 16-pass MFMA needs before its result is read
+__device__ __forceinline__ void pv_drain() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory"); }
+
+// EXACT_LSE: the caller wants the log-sum-exp; it is then summed from the
+// unrounded fp32 probabilities as well (the output is normalised by the sums
+// of the e4m3 values in both forms).
+template <class C, bool EXACT_LSE>
 __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void attn_fwd_fp8_pipe_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __restrict__ Kg,
                               const uint8_t* __restrict__ Vg, uint16_t* __restrict__ Og,
@@ -176,10 +192,14 @@ void attn_fwd_fp8_pipe_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __r
     const char* vb = vslot(j >> 1) + (j & 1) * 64 * 128;
 #pragma unroll
     for (int db = half * 2; db < half * 2 + 2; ++db) {
+      // one lane address per d block; the four reads then differ by constants,
+      // which the barrier keeps out of the sum so they land in the offset field
+      uint32_t a = (uint32_t)(uintptr_t)DIT_LDS(const char, vb) + (uint32_t)v_rd[db];
+      asm volatile("" : "+v"(a));
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const i32x2_t t = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-            DIT_LDS(i32x2_t, (vb + ((u >> 1) * 32 + (u & 1) * 16) * 128 + v_rd[db])));
+            (__attribute__((address_space(3))) i32x2_t*)(uintptr_t)(a + ((u >> 1) * 32 + (u & 1) * 16) * 128));
         vf[db][2 * u] = t[0];
         vf[db][2 * u + 1] = t[1];
       }
@@ -218,9 +238,25 @@ void attn_fwd_fp8_pipe_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __r
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       p[e] = fast_exp2(fmaf(s[b][r0 + e], c_log2, nm));
-      ls += p[e];
+      if constexpr (EXACT_LSE) ls += p[e];
     }
-    pout[w] = (int)pack_e4m3x4(p[0], p[1], p[2], p[3]);
+    // both halves of the word are written, so the first conversion may start
+    // from any register content (an empty asm stands in for it, saving a clear)
+    uint32_t any;
+    asm volatile("" : "=v"(any));
+    const uint32_t lo = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], any, false);
+    pout[w] = (int)__builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], lo, true);
+  };
+  // Row sums of the e4m3 P^T on the matrix core. Read as the B operand of the
+  // 16x16x128 product, lane 16 g + c of a P^T fragment is column c, k-group g;
+  // A holds ones exactly where row r meets k-group r, so output row r, column
+  // c is the sum of the 32 values in lane 16 r + c. Lanes 0..15 receive rows
+  // 0..3: the half-row sums of queries c (rows 0, 2) and c + 16 (rows 1, 3).
+  const int ones_w = (lane & 15) == (lane >> 4) ? 0x38383838 : 0;   // e4m3 1.0
+  const i32x8_t ones = {ones_w, ones_w, ones_w, ones_w, ones_w, ones_w, ones_w, ones_w};
+  auto psum = [&](const i32x8_t& pt) __attribute__((always_inline)) {
+    const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ones, pt, z, 0, 0, 0, 0, 0, 0);
   };
 
   f32x16_t acc[2][4];
@@ -231,9 +267,10 @@ void attn_fwd_fp8_pipe_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __r
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[qb][db][r] = 0.f;
   float mc[2];                        // running row maxima of the scaled logits, log2 units
-  float l_run[2] = {0.f, 0.f};        // sums of 8 p
-  f32x16_t s0[2];                     // raw logits of the current sub-tile, query block 0
-  f32x16_t s1A[2], s1B[2];            // query block 1, alternating between sub-tiles
+  // sums of 8 p in lanes 0..15: query c of each block in l_lo, query c + 16 in l_hi
+  float l_lo[2] = {0.f, 0.f}, l_hi[2] = {0.f, 0.f};
+  float l_ex[2] = {0.f, 0.f};         // EXACT_LSE: this lane's sums of the unrounded 8 p
+  f32x16_t s0[2], s1[2];              // raw logits of the current sub-tile [query block][key block]
   i32x8_t pA[2], pB[2];               // P^T of two consecutive sub-tiles [query block]
 
   // ---- prologue: K tiles u0..u0+2, V tiles u0, u0+1; the first sub-tile's logits
@@ -246,22 +283,24 @@ void attn_fwd_fp8_pipe_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __r
   __syncthreads();
   read_kfrags(2 * u0);
   s_chains(0, s0);
-  s_chains(1, s1A);
-  if (64 * (2 * u0 + 1) > N) { mask_keys(2 * u0, s0); mask_keys(2 * u0, s1A); }
+  s_chains(1, s1);
+  if (64 * (2 * u0 + 1) > N) { mask_keys(2 * u0, s0); mask_keys(2 * u0, s1); }
   mc[0] = row_max(s0);
-  mc[1] = row_max(s1A);
+  mc[1] = row_max(s1);
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) pA[qb] = i32x8_t{};
 #pragma unroll
   for (int db = 0; db < 4; ++db) vf[db] = i32x8_t{};
 
-  // One sub-iteration: consumes P_{j-1} (pin) and S_j (s0, s1in); produces
-  // P_j (pout) and S_{j+1} (s0, s1out).
-  auto sub = [&](int j, i32x8_t (&pin)[2], i32x8_t (&pout)[2], f32x16_t (&s1in)[2], f32x16_t (&s1out)[2],
-                 auto mask_c, auto&& dma) __attribute__((always_inline)) {
+  // One sub-iteration: consumes P_{j-1} (pin) and S_j (s0, s1); produces P_j
+  // (pout) and S_{j+1} (s0, s1), each S block written only after its old
+  // values are consumed.
+  auto sub = [&](int j, i32x8_t (&pin)[2], i32x8_t (&pout)[2], auto mask_c, auto&& dma)
+      __attribute__((always_inline)) {
     constexpr bool MASK = decltype(mask_c)::value;
+    f32x4_t rs0, rs1;
     float ls0 = 0.f, ls1 = 0.f;
-    // ================= phase X
+    // ================= phase X: P_{j-1} V_{j-1}, softmax of S_j block 0
     read_kfrags(j + 1);
     DIT_FENCE();
     {
@@ -269,24 +308,38 @@ void attn_fwd_fp8_pipe_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __r
 #pragma unroll
       for (int st = 0; st < 8; ++st) {
         const int db = st >> 1, qb = st & 1;
-        acc[qb][db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vf[db], pin[qb], acc[qb][db], 0, 0, 0, 0, 0, 0);
+        pv_mfma(acc[qb][db], vf[db], pin[qb]);
         soft_step(s0, st, nm0, pout[0], ls0);
         DIT_FENCE();
       }
     }
-    // ================= phase Y
+    // ================= phase Y: S_{j+1}, softmax of S_j block 1
     {
-      f32x16_t n0[2];
       const float nm1 = kFp8PipePLog2 - mc[1];
-#pragma unroll
-      for (int st = 0; st < 8; ++st) {
-        const int b = st >> 2, qb = (st >> 1) & 1, ks = st & 1;
-        f32x16_t& dst = qb == 0 ? n0[b] : s1out[b];
+      auto smfma = [&](f32x16_t& dst, int b, int qb, int ks) __attribute__((always_inline)) {
         if (ks == 0) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) dst[r] = 0.f;
         }
         dst = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kf[b][ks], qf[qb][ks], dst, 0, 0, 0, 0, 0, 0);
+      };
+#pragma unroll
+      for (int st = 0; st < 8; ++st) {
+        if (st < 4) {
+          smfma(s0[st >> 1], st >> 1, 0, st & 1);          // block 0 (consumed in phase X)
+          if (st == 0) rs0 = psum(pout[0]);
+        } else if (st < 6) {
+          soft_step(s1, st, nm1, pout[1], ls1);            // key block 0 of S_j block 1 is free after
+          smfma(s1[0], 0, 1, st - 4);                      // words 0-3 (steps 0-3)
+        } else if (st == 6) {
+          soft_step(s1, 6, nm1, pout[1], ls1);
+          soft_step(s1, 7, nm1, pout[1], ls1);
+          smfma(s1[1], 1, 1, 0);
+        } else {
+          smfma(s1[1], 1, 1, 1);
+          rs1 = psum(pout[1]);
+        }
+        if (st < 4) soft_step(s1, st, nm1, pout[1], ls1);
         // the V_j fragment reads go behind the first MFMAs (the K fragments
         // were read a phase earlier); 8 at a time, lgkmcnt counts at most 15
         if (st < 2) {
@@ -294,47 +347,76 @@ void attn_fwd_fp8_pipe_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __r
           read_vfrags(j, st);
           DIT_FENCE();
         }
-        soft_step(s1in, st, nm1, pout[1], ls1);
         if (st >= 4) dma(st - 4);
         DIT_FENCE();
       }
       if constexpr (MASK) {
-        if (64 * (j + 2) > N) { mask_keys(j + 1, n0); mask_keys(j + 1, s1out); }
+        if (64 * (j + 2) > N) { mask_keys(j + 1, s0); mask_keys(j + 1, s1); }
       }
-      s0[0] = n0[0];
-      s0[1] = n0[1];
     }
     // The packed P must exist here: without this the compiler sinks the e4m3
     // conversions past the rare-path branch, out of the MFMA phases.
     asm volatile("" ::"v"(pout[0]), "v"(pout[1]));
-    // ---- rare path: some lane's p reached the e4m3 range limit
-    const bool bad = !(ls0 <= kFp8PipeSumLimit) || !(ls1 <= kFp8PipeSumLimit);
-    if (__builtin_amdgcn_ballot_w64(bad) != 0) {
-      read_kfrags(j);                      // K tile j/2 is still in its slot
-      ls0 = 0.f;
-      ls1 = 0.f;
+    // ---- rare path: some p reached the e4m3 range limit (a saturated 448, or
+    // a NaN, makes its half-row sum fail the test)
+    // The sums are >= +0 or NaN, so their bit patterns order like the values
+    // (a NaN above every finite one): an unsigned maximum needs no NaN care.
+    auto u = [](float x) { return __float_as_uint(x); };
+    const uint32_t big = max(max(max(u(rs0[0]), u(rs0[1])), max(u(rs0[2]), u(rs0[3]))),
+                             max(max(u(rs1[0]), u(rs1[1])), max(u(rs1[2]), u(rs1[3]))));
+    if (__builtin_amdgcn_ballot_w64(big >= u(kFp8PipeSumLimit)) != 0) {
+      // Recompute S_j from K in LDS into the registers of S_{j+1}, take its
+      // exact row maxima, rescale, redo P_j; then recompute S_{j+1}. Reusing
+      // those registers keeps this path's working set to one accumulator
+      // block, which keeps it from crowding the steady loop's registers.
+      DIT_FENCE();
+      read_kfrags(j);                      // K tiles j/2 and (j+1)/2 are still in their slots
+      s_chains(0, s0);
+      s_chains(1, s1);
+      if constexpr (MASK) {
+        if (64 * (j + 1) > N) { mask_keys(j, s0); mask_keys(j, s1); }
+      }
+      DIT_FENCE();
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
-        f32x16_t s[2];
-        s_chains(qb, s);
-        if constexpr (MASK) {
-          if (64 * (j + 1) > N) mask_keys(j, s);
-        }
+        const f32x16_t (&s)[2] = qb == 0 ? s0 : s1;
         const float m_new = fmaxf(mc[qb], row_max(s));
         const float alpha = fast_exp2(mc[qb] - m_new);
-        l_run[qb] *= alpha;
+        l_lo[qb] *= __shfl(alpha, lane & 15);
+        l_hi[qb] *= __shfl(alpha, (lane & 15) + 16);
+        l_ex[qb] *= alpha;
 #pragma unroll
-        for (int db = 0; db < 4; ++db)
+        for (int db = 0; db < 4; ++db) {          // one block at a time, AGPRs to AGPRs
+          asm volatile("" : "+a"(acc[qb][db]));
 #pragma unroll
           for (int r = 0; r < 16; ++r) acc[qb][db][r] *= alpha;
+          asm volatile("" : "+a"(acc[qb][db]));
+          DIT_FENCE();
+        }
         mc[qb] = m_new;
         const float nm = kFp8PipePLog2 - m_new;
+        float& ls = qb == 0 ? ls0 : ls1;
+        ls = 0.f;
 #pragma unroll
-        for (int w = 0; w < 8; ++w) soft_step(s, w, nm, pout[qb], qb == 0 ? ls0 : ls1);
+        for (int w = 0; w < 8; ++w) soft_step(s, w, nm, pout[qb], ls);
+        DIT_FENCE();
       }
+      rs0 = psum(pout[0]);
+      rs1 = psum(pout[1]);
+      read_kfrags(j + 1);
+      s_chains(0, s0);
+      s_chains(1, s1);
+      if constexpr (MASK) {
+        if (64 * (j + 2) > N) { mask_keys(j + 1, s0); mask_keys(j + 1, s1); }
+      }
+      DIT_FENCE();
     }
-    l_run[0] += ls0;
-    l_run[1] += ls1;
+    l_ex[0] += ls0;
+    l_ex[1] += ls1;
+    l_lo[0] += rs0[0] + rs0[2];
+    l_hi[0] += rs0[1] + rs0[3];
+    l_lo[1] += rs1[0] + rs1[2];
+    l_hi[1] += rs1[1] + rs1[3];
   };
 
   // One 128-key tile u: streams in K tile u+3 (first sub-iteration) and V tile
@@ -348,13 +430,13 @@ void attn_fwd_fp8_pipe_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __r
     const char* sv = vslot(u + 2);
     DIT_FENCE();
     static_assert(C::kDmaPerWave == 5, "DMA hook spreads 5 instructions over 4 steps");
-    sub(2 * u, pA, pB, s1A, s1B, tail_c, [&](int st) __attribute__((always_inline)) {
+    sub(2 * u, pA, pB, tail_c, [&](int st) __attribute__((always_inline)) {
       if (k_next) {
         dma_one(rk, sk, kdo, st);
         if (st == 0) dma_one(rk, sk, kdo, 4);
       }
     });
-    sub(2 * u + 1, pB, pA, s1B, s1A, tail_c, [&](int st) __attribute__((always_inline)) {
+    sub(2 * u + 1, pB, pA, tail_c, [&](int st) __attribute__((always_inline)) {
       if (v_next) {
         dma_one(rv, sv, vdo, st);
         if (st == 0) dma_one(rv, sv, vdo, 4);
@@ -377,13 +459,20 @@ void attn_fwd_fp8_pipe_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __r
   for (int db = 0; db < 4; ++db)
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb)
-      acc[qb][db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vf[db], pA[qb], acc[qb][db], 0, 0, 0, 0, 0, 0);
+      pv_mfma(acc[qb][db], vf[db], pA[qb]);
+  pv_drain();
 
-  // l_run sums 8 p, and so does acc: their ratio needs no further scaling
+  // l sums 8 p, and so does acc: their ratio needs no further scaling
+  float l_q[2];                        // the row sum of this lane's query
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const float lo = __shfl(l_lo[qb], l32 & 15), hi = __shfl(l_hi[qb], l32 & 15);
+    l_q[qb] = l32 < 16 ? lo : hi;
+  }
   if (ws_index >= 0) {
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-      const float l_tot = pair_sum(l_run[qb]);
+      const float l_tot = l_q[qb];
       const float mul = dv / l_tot;
       const int r = wave * 64 + qb * 32 + l32;
       float* orow = split.ws_o + ((size_t)ws_index * C::kBR + r) * D;
@@ -397,13 +486,18 @@ void attn_fwd_fp8_pipe_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __r
           *(f32x4_t*)(orow + d0) = w;
         }
       if (hh == 0) split.ws_lse[(size_t)ws_index * C::kBR + r] = mc[qb] + __log2f(l_tot) - kFp8PipePLog2;
+      if constexpr (EXACT_LSE) {
+        const float l_exact = pair_sum(l_ex[qb]);
+        if (hh == 0) split.ws_lse_out[(size_t)ws_index * C::kBR + r] = mc[qb] + __log2f(l_exact) - kFp8PipePLog2;
+      }
     }
     return;
   }
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
-    const float l_tot = pair_sum(l_run[qb]);
+    const float l_tot = l_q[qb];
     const float mul = dv / l_tot;
+    const float l_exact = EXACT_LSE ? pair_sum(l_ex[qb]) : 0.f;
     const int row = q0 + qb * 32 + l32;
     if (row < N) {
       uint16_t* orow = Og + base + (size_t)row * D;
@@ -417,8 +511,8 @@ void attn_fwd_fp8_pipe_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __r
           w.y = pack_bf16x2(acc[qb][db][i * 4 + 2] * mul, acc[qb][db][i * 4 + 3] * mul);
           *(uint2*)(orow + d0) = w;
         }
-      if (LSEg != nullptr && hh == 0)
-        LSEg[(size_t)bh * N + row] = (mc[qb] + __log2f(l_tot) - kFp8PipePLog2) * 0.6931471805599453f;
+      if (EXACT_LSE && hh == 0)
+        LSEg[(size_t)bh * N + row] = (mc[qb] + __log2f(l_exact) - kFp8PipePLog2) * 0.6931471805599453f;
     }
   }
 }

@@ -44,7 +44,10 @@ hipError_t allow_lds_pipe() {
 }
 template <class C>
 hipError_t allow_lds_fp8() {
-  return hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_fwd_fp8_pipe_kernel<C>),
+  const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_fwd_fp8_pipe_kernel<C, false>),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, C::kLdsBytes);
+  if (e != hipSuccess) return e;
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_fwd_fp8_pipe_kernel<C, true>),
                              hipFuncAttributeMaxDynamicSharedMemorySize, C::kLdsBytes);
 }
 
@@ -181,9 +184,12 @@ int launch_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
   void* ws = nullptr;
   if (plan_split(BH, n_qtiles, N, C::kKB, n_cu, &sp)) {
     const size_t units = (size_t)sp.n_split * sp.parts * C::kBR;
-    if (hipMallocAsync(&ws, units * (C::kD + 1) * sizeof(float), st) == hipSuccess && ws != nullptr) {
+    // O's merge weights come from the e4m3 sums; an LSE output has exact sums of its own
+    const size_t floats = units * (C::kD + 1) + (lse != nullptr ? units : 0);
+    if (hipMallocAsync(&ws, floats * sizeof(float), st) == hipSuccess && ws != nullptr) {
       sp.ws_o = static_cast<float*>(ws);
       sp.ws_lse = sp.ws_o + units * C::kD;
+      sp.ws_lse_out = lse != nullptr ? sp.ws_lse + units : nullptr;
     } else {
       (void)hipGetLastError();
       ws = nullptr;
@@ -191,7 +197,8 @@ int launch_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
     }
   }
   const long long grid = (long long)sp.n_full + (long long)sp.n_split * sp.parts;
-  hipLaunchKernelGGL(attn_fwd_fp8_pipe_kernel<C>, dim3((unsigned)grid), dim3(C::kThreads), C::kLdsBytes, st,
+  auto* kernel = lse != nullptr ? &attn_fwd_fp8_pipe_kernel<C, true> : &attn_fwd_fp8_pipe_kernel<C, false>;
+  hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(C::kThreads), C::kLdsBytes, st,
                      static_cast<const uint8_t*>(q), static_cast<const uint8_t*>(k),
                      static_cast<const uint8_t*>(v), static_cast<uint16_t*>(o), lse, descale, N, n_qtiles,
                      scale_log2, scale, sp);

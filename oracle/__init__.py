@@ -18,7 +18,8 @@ Pins (what each function is checked against, in tests/test_oracle*.py):
 * ``quantize_per_tensor``: absmax code is 448, scale round trip, torch cast.
 * ``attention_fp8_pipeline``: with P unrounded it equals ``attention`` on the
   dequantised inputs; the P rounding error obeys the e4m3 bound; closed forms
-  with identical keys and N = 1.
+  with identical keys and N = 1; with the rounded denominator a constant V is
+  returned exactly and rows differ from the default by one bounded factor.
 """
 from .attention import attention, attention_bruteforce, softmax_probabilities
 from .formats import (E4M3_MAX, bf16_round, e4m3_decode, e4m3_encode,

@@ -6,8 +6,11 @@ third paragraph; English card, "Key takeaways"): Q, K and V are each
 quantised per tensor to e4m3 with an absmax scale, the logits are formed
 from the e4m3 values and rescaled by dq*dk*scale, the softmax probabilities
 p (relative to the row maximum) are multiplied by 2^8 and rounded to e4m3
-before the second contraction, the row sum l is taken from the unrounded p,
-and the output is (P8 V8) * dv / (2^8 * l).
+before the second contraction, and the output is (P8 V8) * dv / (2^8 * l).
+The pages leave l open. Two readings are provided: l from the unrounded p
+(the default), or l from the rounded P8 themselves (``den_rounded=True``),
+which makes every output row an exact convex combination of rows of V8. The
+log-sum-exp returned is always the exact one, m + log(sum p).
 
 Everything here is evaluated exactly in float64 apart from the two e4m3
 roundings the pipeline itself prescribes (inputs, and P).
@@ -22,7 +25,7 @@ P_SCALE = 256.0
 
 
 def attention_fp8_pipeline(q8, k8, v8, dq, dk, dv, scale, rows=None, block=512,
-                           p_scale=P_SCALE, round_p=True):
+                           p_scale=P_SCALE, round_p=True, den_rounded=False):
     """Return (O, lse) of the emulated fp8 pipeline, float64.
 
     q8, k8, v8: uint8 e4m3 codes of shape (B, H, N, d). ``round_p=False``
@@ -47,7 +50,8 @@ def attention_fp8_pipeline(q8, k8, v8, dq, dk, dv, scale, rows=None, block=512,
                 den = p.sum(axis=1, keepdims=True)
                 if round_p:
                     p8 = e4m3_decode(e4m3_encode(p * p_scale))
-                    o = (p8 @ v[b, h]) * np.float64(dv) / (p_scale * den)
+                    l8 = p8.sum(axis=1, keepdims=True) if den_rounded else p_scale * den
+                    o = (p8 @ v[b, h]) * np.float64(dv) / l8
                 else:
                     o = (p @ v[b, h]) * np.float64(dv) / den
                 out[b, h, r0:r0 + sel.size] = o

@@ -127,6 +127,27 @@ def test_fp8_pipeline_p_rounding_within_e4m3_bound():
     assert np.abs(o - o0).max() > 0          # the rounding is really applied
 
 
+def test_fp8_pipeline_rounded_denominator():
+    """den_rounded divides by the sum of the rounded P8: a constant V comes back
+    exactly (a convex combination), and each row differs from the default
+    reading by one factor, the ratio of the two sums, within the e4m3 bound."""
+    (q8, dq, _), (k8, dk, _), (v8, dv, _) = _fp8_inputs(1, 2, 150, 32, 8)
+    scale = 1 / math.sqrt(32)
+    o_r, lse_r = oracle.attention_fp8_pipeline(q8, k8, v8, dq, dk, dv, scale, den_rounded=True)
+    o_e, lse_e = oracle.attention_fp8_pipeline(q8, k8, v8, dq, dk, dv, scale)
+    assert np.array_equal(lse_r, lse_e)                  # the log-sum-exp stays the exact one
+    big = np.abs(o_e) > 1e-3
+    ratio = np.where(big, o_r / np.where(big, o_e, 1.0), np.nan)
+    row_ratio = np.nanmedian(ratio, axis=3, keepdims=True)
+    assert np.allclose(np.where(big, ratio, row_ratio), row_ratio, rtol=1e-9, atol=0)
+    assert np.abs(row_ratio - 1).max() <= 2.0**-4 and np.abs(row_ratio - 1).max() > 0
+    c8 = np.full_like(v8, 0x3C)                          # e4m3 1.5
+    o_c, _ = oracle.attention_fp8_pipeline(q8, k8, c8, dq, dk, dv, scale, den_rounded=True)
+    assert np.allclose(o_c, 1.5 * np.float64(dv), rtol=1e-15, atol=0)
+    o_c0, _ = oracle.attention_fp8_pipeline(q8, k8, c8, dq, dk, dv, scale)
+    assert np.abs(o_c0 - 1.5 * np.float64(dv)).max() > 1e-6
+
+
 def test_fp8_pipeline_closed_forms():
     (q8, dq, _), (k8, dk, _), (v8, dv, _) = _fp8_inputs(1, 1, 64, 16, 7)
     k8 = np.broadcast_to(k8[:, :, :1], k8.shape).copy()          # identical keys: p = 1 exactly
