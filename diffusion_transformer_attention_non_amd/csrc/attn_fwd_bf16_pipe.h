@@ -190,23 +190,24 @@ void attn_fwd_bf16_pipe_kernel(const uint16_t* __restrict__ Qg, const uint16_t* 
   const int g = lane >> 4, gi = lane & 15;
   const int v_rd = ((g >> 1) * 4 + (gi >> 2)) * VROW + (g & 1) * 32 + (gi & 3) * 8;
   bf16x8_t kf[KS];
+  auto kbase = [&](int j) { return kslot(j >> 1) + (j & 1) * 32 * KROW + k_rd; };
+  auto read_kfrag = [&](const char* kb, int ks) __attribute__((always_inline)) {
+    kf[ks] = __builtin_bit_cast(bf16x8_t, *(const i32x4_t*)(kb + ks * 32));
+  };
   auto read_kfrags = [&](int j) {
-    const char* kb = kslot(j >> 1) + (j & 1) * 32 * KROW + k_rd;
+    const char* kb = kbase(j);
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) kf[ks] = __builtin_bit_cast(bf16x8_t, *(const i32x4_t*)(kb + ks * 32));
+    for (int ks = 0; ks < KS; ++ks) read_kfrag(kb, ks);
   };
   bf16x8_t vf[2][DB];
-  auto read_vfrags = [&](int j, int half) {
-    const char* vb = vslot(j >> 1) + (j & 1) * 32 * VROW + half * 16 * VROW + v_rd;
-#pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      const char* p = vb + db * 64;
-      const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(DIT_LDS(i16x4_t, p));
-      const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(DIT_LDS(i16x4_t, (p + 8 * VROW)));
-      const i32x2_t lo2 = __builtin_bit_cast(i32x2_t, lo), hi2 = __builtin_bit_cast(i32x2_t, hi);
-      const i32x4_t a4 = {lo2[0], lo2[1], hi2[0], hi2[1]};
-      vf[half][db] = __builtin_bit_cast(bf16x8_t, a4);
-    }
+  auto vbase = [&](int j) { return vslot(j >> 1) + (j & 1) * 32 * VROW + v_rd; };
+  auto read_vfrag = [&](const char* vb, int half, int db) __attribute__((always_inline)) {
+    const char* p = vb + half * 16 * VROW + db * 64;
+    const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(DIT_LDS(i16x4_t, p));
+    const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(DIT_LDS(i16x4_t, (p + 8 * VROW)));
+    const i32x2_t lo2 = __builtin_bit_cast(i32x2_t, lo), hi2 = __builtin_bit_cast(i32x2_t, hi);
+    const i32x4_t a4 = {lo2[0], lo2[1], hi2[0], hi2[1]};
+    vf[half][db] = __builtin_bit_cast(bf16x8_t, a4);
   };
   // keys of sub-tile j past N do not exist
   auto mask_keys = [&](int j, f32x16_t& s) {
@@ -229,26 +230,23 @@ void attn_fwd_bf16_pipe_kernel(const uint16_t* __restrict__ Qg, const uint16_t* 
     return pair_max(mx) * scale_log2;      // scale_log2 > 0
   };
   // P = 2^t for 8 consecutive entries of t, packed to bf16
-  auto exp_half = [&](const f32x16_t& t, int half, bf16x8_t& out) {
-    i32x4_t w;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const bf16x2_t pk = {(__bf16)fast_exp2(t[half * 8 + 2 * e]), (__bf16)fast_exp2(t[half * 8 + 2 * e + 1])};
-      w[e] = __builtin_bit_cast(int, pk);
-    }
-    out = __builtin_bit_cast(bf16x8_t, w);
+  // p = 2^t[i], summed unrounded into ls; pack_word puts two p as bf16 word
+  // e & 3 of out[e >> 2]. (Row sums with v_dot2 on the packed P would
+  // wait for the matrix core each time: dot instructions issue behind the
+  // MFMA in flight.)
+  auto exp_one = [&](const f32x16_t& t, int i, float& ls) __attribute__((always_inline)) {
+    const float p = fast_exp2(t[i]);
+    ls += p;
+    asm volatile("" : "+v"(ls));       // keeps the add in this step
+    return p;
   };
-  const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
-  auto rowsum = [&](const bf16x8_t& p, float acc_s) {
-    const i32x4_t w = __builtin_bit_cast(i32x4_t, p);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      // the element goes through a scalar first: hipcc miscompiles a bit_cast
-      // whose operand is an element of an ext_vector (it reads element 0)
-      const int x = w[e];
-      acc_s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, x), ones, acc_s, false);
-    }
-    return acc_s;
+  auto pack_word = [&](float a, float b, int e, bf16x8_t (&out)[2]) __attribute__((always_inline)) {
+    const bf16x2_t pk = {(__bf16)a, (__bf16)b};
+    int word = __builtin_bit_cast(int, pk);
+    asm volatile("" : "+v"(word));     // keeps the pack in this step
+    i32x4_t w = __builtin_bit_cast(i32x4_t, out[e >> 2]);
+    w[e & 3] = word;
+    out[e >> 2] = __builtin_bit_cast(bf16x8_t, w);
   };
 
   f32x16_t acc[2][DB];
@@ -284,6 +282,7 @@ void attn_fwd_bf16_pipe_kernel(const uint16_t* __restrict__ Qg, const uint16_t* 
 #pragma unroll
     for (int r = 0; r < 16; ++r) t0[r] = fmaf(s0[r], scale_log2, -mc[0]);
   }
+  read_kfrags(2 * u0 + 1);          // the K fragments a sub-iteration starts with are those of the next sub-tile
   // the first phase X adds 0 * 0: no previous sub-tile yet
 #pragma unroll
   for (int h = 0; h < 2; ++h)
@@ -294,85 +293,84 @@ void attn_fwd_bf16_pipe_kernel(const uint16_t* __restrict__ Qg, const uint16_t* 
 #pragma unroll
     for (int db = 0; db < DB; ++db) vf[h][db] = bf16x8_t{};
 
-  // One sub-iteration: consumes P_{j-1} (pin), produces P_j (pout).
+  // One sub-iteration j. On entry: P_{j-1} (pin), V_{j-1} fragments (vf),
+  // K_{j+1} fragments (kf), S_j's exponent arguments for query block 0 (t0)
+  // and raw logits for query block 1 (s1). Two phases of 8 steps; each step
+  // is one P V MFMA (independent accumulators) and one S_{j+1} MFMA (a chain),
+  // with half of the same VALU mix behind each: two exponentials of P_j with
+  // their row-sum adds and bf16 pack, and two FMAs. The LDS reads of the next
+  // fragments follow the MFMA that last reads the register: V_j during both
+  // phases, K_{j+2} during phase Y. On exit the state holds sub-tile j+1.
   // MASK: keys of S_{j+1} (and, on the rare path, of S_j) may lie past N.
-  // dma(st) issues this sub-iteration's share of the tile DMA at phase-Y step st.
+  // dma(m) issues this sub-iteration's share of the tile DMA at phase-X step 2 m.
   auto sub = [&](int j, bf16x8_t (&pin)[2][2], bf16x8_t (&pout)[2][2], auto mask_c, auto&& dma)
       __attribute__((always_inline)) {
     constexpr bool MASK = decltype(mask_c)::value;
-    // ================= phase X
-    read_kfrags(j + 1);
-    DIT_FENCE();
+    float ls0 = 0.f, ls1 = 0.f;
+    f32x16_t& t1 = s1;         // in place
+    f32x16_t sa, sb;           // S_{j+1} of query blocks 0 and 1
+    const char* vb = vbase(j);
+    const char* kb2 = kbase(j + 2);
+    // ================= phase X: P_{j-1} V_{j-1} (keys 0-15), S_{j+1} block 0, P_j block 0
     {
       const float m1 = mc[1];
-      f32x16_t& t1 = s1;       // in place
 #pragma unroll
       for (int st = 0; st < 8; ++st) {
-        const int half = st >> 2, db = st & 3;
+        const int qb = st & 1, db = st >> 1;
+        acc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[0][db], pin[qb][0], acc[qb][db], 0, 0, 0);
+        t1[2 * st] = fmaf(s1[2 * st], scale_log2, -m1);
+        t1[2 * st + 1] = fmaf(s1[2 * st + 1], scale_log2, -m1);
+        const float pa = exp_one(t0, 2 * st, ls0);
+        if ((st & 1) == 0) dma(st >> 1);
+        DIT_FENCE();
+        if (st == 0) {
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
-          acc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[half][db], pin[qb][half], acc[qb][db], 0, 0, 0);
-        if (st < 4) {
-#pragma unroll
-          for (int r = st * 4; r < st * 4 + 4; ++r) t1[r] = fmaf(s1[r], scale_log2, -m1);
+          for (int r = 0; r < 16; ++r) sa[r] = 0.f;
         }
-        if (st == 1) exp_half(t0, 0, pout[0][0]);
-        if (st == 3) exp_half(t0, 1, pout[0][1]);
-        if (st == 5) exp_half(t1, 0, pout[1][0]);
-        if (st == 7) exp_half(t1, 1, pout[1][1]);
+        sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[st], qf[0][st], sa, 0, 0, 0);
+        const float pb = exp_one(t0, 2 * st + 1, ls0);
+        pack_word(pa, pb, st, pout[0]);
+        if (st & 1) read_vfrag(vb, 0, db);      // both query blocks have used vf[0][db]
         DIT_FENCE();
       }
     }
-    // ================= phase Y
-    float ls0 = 0.f, ls1 = 0.f;
+    if constexpr (MASK) {
+      if (32 * (j + 2) > N) mask_keys(j + 1, sa);
+    }
+    // ================= phase Y: P_{j-1} V_{j-1} (keys 16-31), S_{j+1} block 1, P_j block 1
     {
-      f32x16_t sa, sb;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) { sa[r] = 0.f; sb[r] = 0.f; }
-      // steps 0-3: S_{j+1} of query block 0, with the row sums of P_j
-#pragma unroll
-      for (int st = 0; st < 4; ++st) {
-#pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2)
-          sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[st * 2 + k2], qf[0][st * 2 + k2], sa, 0, 0, 0);
-        // the V_j fragment reads go behind the first MFMAs, which then wait
-        // for nothing (the K fragments were read a phase earlier); at most 8
-        // at a time, since lgkmcnt counts no more than 15 outstanding reads
-        if (st < 2) {
-          DIT_FENCE();
-          read_vfrags(j, st);
-          DIT_FENCE();
-        }
-        if (st == 0) ls0 = rowsum(pout[0][0], ls0);
-        if (st == 1) ls0 = rowsum(pout[0][1], ls0);
-        if (st == 2) ls1 = rowsum(pout[1][0], ls1);
-        if (st == 3) ls1 = rowsum(pout[1][1], ls1);
-        DIT_FENCE();
-      }
-      if constexpr (MASK) {
-        if (32 * (j + 2) > N) mask_keys(j + 1, sa);
-      }
       const float m0 = mc[0];
-      // steps 4-7: query block 1, with the exponent arguments of block 0
 #pragma unroll
-      for (int st = 0; st < 4; ++st) {
+      for (int st = 0; st < 8; ++st) {
+        const int qb = st & 1, db = st >> 1;
+        acc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[1][db], pin[qb][1], acc[qb][db], 0, 0, 0);
+        t0[2 * st] = fmaf(sa[2 * st], scale_log2, -m0);        // S_{j+1}'s arguments
+        t0[2 * st + 1] = fmaf(sa[2 * st + 1], scale_log2, -m0);
+        const float pa = exp_one(t1, 2 * st, ls1);
+        DIT_FENCE();
+        if (st == 0) {
 #pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2)
-          sb = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[st * 2 + k2], qf[1][st * 2 + k2], sb, 0, 0, 0);
-#pragma unroll
-        for (int r = st * 4; r < st * 4 + 4; ++r) t0[r] = fmaf(sa[r], scale_log2, -m0);
-        dma(st);
+          for (int r = 0; r < 16; ++r) sb[r] = 0.f;
+        }
+        sb = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[st], qf[1][st], sb, 0, 0, 0);
+        const float pb = exp_one(t1, 2 * st + 1, ls1);
+        pack_word(pa, pb, st, pout[1]);
+        read_kfrag(kb2, st);                     // kf[st] is free: K_{j+2}
+        if (st & 1) read_vfrag(vb, 1, db);
         DIT_FENCE();
       }
-      if constexpr (MASK) {
-        if (32 * (j + 2) > N) mask_keys(j + 1, sb);
-      }
-      s1 = sb;
     }
+    if constexpr (MASK) {
+      if (32 * (j + 2) > N) mask_keys(j + 1, sb);
+    }
+    s1 = sb;
+    // The packed P must exist here: without this the compiler sinks the bf16
+    // packs past the rare-path branch, out of the MFMA phases.
+    asm volatile("" ::"v"(pout[0][0]), "v"(pout[0][1]), "v"(pout[1][0]), "v"(pout[1][1]));
     // ---- rare path: a probability of sub-tile j exceeded 2^8
     const bool bad = !(ls0 <= kPipeSumLimit) || !(ls1 <= kPipeSumLimit);
     if (__builtin_amdgcn_ballot_w64(bad) != 0) {
-      read_kfrags(j);                      // K tile j/2 is still in its slot
+      read_kfrags(j);                      // K tiles j/2 and (j+2)/2 are still in their slots
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
         f32x16_t s;
@@ -395,19 +393,23 @@ void attn_fwd_bf16_pipe_kernel(const uint16_t* __restrict__ Qg, const uint16_t* 
         mc[qb] = m_new;
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[r] = fmaf(s[r], scale_log2, -m_new);
-        exp_half(s, 0, pout[qb][0]);
-        exp_half(s, 1, pout[qb][1]);
+        float& ls = qb == 0 ? ls0 : ls1;
+        ls = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float pa = exp_one(s, 2 * e, ls);
+          pack_word(pa, exp_one(s, 2 * e + 1, ls), e, pout[qb]);
+        }
       }
-      ls0 = rowsum(pout[0][1], rowsum(pout[0][0], 0.f));
-      ls1 = rowsum(pout[1][1], rowsum(pout[1][0], 0.f));
+      read_kfrags(j + 2);
     }
     l_run[0] += ls0;
     l_run[1] += ls1;
   };
 
   // One 64-key tile u. It streams in K tile u+3 (during its first
-  // sub-iteration) and V tile u+2 (during its second), one DMA instruction per
-  // phase-Y step, and then waits for the tiles issued one iteration earlier
+  // sub-iteration) and V tile u+2 (during its second), one DMA instruction on
+  // every other phase-X step, and then waits for the tiles issued one iteration earlier
   // (K u+2, V u+1) before the barrier that publishes them. In the steady
   // state (TAIL false) both DMAs exist and no key of tiles u, u+1 lies past N,
   // so the body has no branch but the rare path: a branch would let the
