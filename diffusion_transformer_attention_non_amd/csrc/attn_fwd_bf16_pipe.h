@@ -369,7 +369,7 @@ void attn_fwd_bf16_pipe_kernel(const uint16_t* __restrict__ Qg, const uint16_t* 
     asm volatile("" ::"v"(pout[0][0]), "v"(pout[0][1]), "v"(pout[1][0]), "v"(pout[1][1]));
     // ---- rare path: a probability of sub-tile j exceeded 2^8
     const bool bad = !(ls0 <= kPipeSumLimit) || !(ls1 <= kPipeSumLimit);
-    if (__builtin_amdgcn_ballot_w64(bad) != 0) {
+    if (__builtin_expect(__builtin_amdgcn_ballot_w64(bad) != 0, 0)) {
       read_kfrags(j);                      // K tiles j/2 and (j+2)/2 are still in their slots
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {

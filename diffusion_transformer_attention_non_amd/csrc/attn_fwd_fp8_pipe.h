@@ -336,8 +336,11 @@ void attn_fwd_fp8_pipe_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __r
           soft_step(s1, 7, nm1, pout[1], ls1);
           smfma(s1[1], 1, 1, 0);
         } else {
-          smfma(s1[1], 1, 1, 1);
+          // ahead of the last S MFMA, so that the sums are ready when the
+          // saturation test reads them
           rs1 = psum(pout[1]);
+          DIT_FENCE();
+          smfma(s1[1], 1, 1, 1);
         }
         if (st < 4) soft_step(s1, st, nm1, pout[1], ls1);
         // the V_j fragment reads go behind the first MFMAs (the K fragments
@@ -437,16 +440,15 @@ void attn_fwd_fp8_pipe_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __r
       }
     });
     sub(2 * u + 1, pB, pA, tail_c, [&](int st) __attribute__((always_inline)) {
-      if (v_next) {
-        dma_one(rv, sv, vdo, st);
-        if (st == 0) dma_one(rv, sv, vdo, 4);
-      }
+      // a V tile is 16 KB: instructions 16-19 (m = 4) would only zero-fill
+      // rows that are never read
+      if (v_next) dma_one(rv, sv, vdo, st);
     });
     DIT_FENCE();
     if (TAIL)
       __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     else
-      __builtin_amdgcn_s_waitcnt(0x0F7A);  // vmcnt(10): this iteration's 10 DMAs may stay in flight
+      __builtin_amdgcn_s_waitcnt(0x0F79);  // vmcnt(9): this iteration's 9 DMAs (5 K, 4 V) may stay in flight
     __syncthreads();
     DIT_FENCE();
   };

@@ -91,3 +91,17 @@ def test_valid_call_without_gpu_reports_device_error(lib):
     if torch.cuda.is_available():
         pytest.skip("a GPU is present; covered by the GPU tests")
     assert lib.dit_attn_fwd(A, B_, C, O, 1, 1, 8, 64, 0.125, 0, None) == -3
+
+
+def test_build_refuses_spilling_attention_kernels():
+    """The build reads hipcc's per-kernel resource report and refuses an
+    attention kernel with scratch (spill) bytes; other kernels may spill."""
+    from diffusion_transformer_attention_non_amd.build import check_no_spills
+    ok = ("a.h:1:1: remark: Function Name: _ZN7ditattn24attn_fwd_fp8_pipe_kernelX [-Rpass-analysis=kernel-resource-usage]\n"
+          "a.h:1:1: remark:     ScratchSize [bytes/lane]: 0 [-Rpass-analysis=kernel-resource-usage]\n"
+          "b.h:1:1: remark: Function Name: _ZN7ditattn17quant_e4m3_kernelX [-Rpass-analysis=kernel-resource-usage]\n"
+          "b.h:1:1: remark:     ScratchSize [bytes/lane]: 64 [-Rpass-analysis=kernel-resource-usage]\n")
+    check_no_spills(ok)
+    bad = ok.replace("ScratchSize [bytes/lane]: 0", "ScratchSize [bytes/lane]: 384")
+    with pytest.raises(RuntimeError, match="attn_fwd_fp8_pipe_kernelX: 384"):
+        check_no_spills(bad)
