@@ -16,27 +16,28 @@
 // padding are pointed past the tile, so the range check zero-fills them
 // without a memory access. K lives in a ring of 4 tile slots and V in a ring
 // of 3: while tile u is computed on, K tile u+3 and V tile u+2 stream in (one
-// DMA instruction per MFMA step of phase Y), and one s_waitcnt + barrier per
-// 64 keys publishes the tiles issued an iteration earlier.
+// DMA instruction on every other step of phase X), and one s_waitcnt +
+// barrier per 64 keys publishes the tiles issued an iteration earlier.
 //
-// Sub-iteration j (32 keys), two phases of 16 MFMAs each:
-//   X: O^T += V_{j-1}^T P_{j-1}^T, interleaved with the exponent arguments of
-//      S_j's second query block and P_j = 2^t packed to bf16; the K_{j+1}
-//      fragment reads are issued first.
-//   Y: S_{j+1} = K_{j+1} Q^T (two chains of 8 MFMAs), interleaved with the row
-//      sums of P_j (v_dot2_f32_bf16 on the packed values), the exponent
-//      arguments of S_{j+1}'s first block and the V_j fragment reads.
-// P alternates between two register sets over the two sub-iterations of a
-// tile, so nothing is copied at the loop edge.
+// Sub-iteration j (32 keys), two phases of 8 steps. Each step is one
+// O^T += V_{j-1}^T P_{j-1}^T MFMA and one S_{j+1} = K_{j+1} Q^T MFMA (a chain
+// over d), with half of a fixed VALU mix behind each MFMA: two exponentials
+// of P_j with their row-sum adds and one bf16 pack, and two FMAs forming
+// exponent arguments (of S_j's second query block in phase X, of S_{j+1}'s
+// first in phase Y). Fragment reads from LDS follow the MFMA that last reads
+// the register they fill: V_j over both phases, K_{j+2} over phase Y. P
+// alternates between two register sets over the two sub-iterations of a
+// tile, so nothing is copied at the loop edge. Row sums are fp32 adds: a
+// v_dot2 on the packed P would issue only after the MFMA in flight.
 //
 // Softmax without a per-tile maximum. The running maximum m (log2 units, per
-// query row) starts at the exact maximum of the first 32 keys and only moves
-// when a sub-tile's probabilities, relative to m, sum to more than 2^8 in
-// some lane. That rare path recomputes the sub-tile's logits from K (still in
-// LDS), takes their exact maximum, rescales O and l and recomputes P. Every
-// probability otherwise stays below 2^8. Row sums come from the bf16-rounded
-// probabilities, so each row of O is normalised by exactly the weights its
-// MFMAs used.
+// query row) starts at the exact maximum of the first 32 keys. bf16 keeps
+// 8 significant bits at any scale, so probabilities relative to a stale m lose
+// nothing as long as nothing overflows: m moves only when a lane's sum of a
+// sub-tile's probabilities exceeds 2^64 (or is not finite). That rare path
+// recomputes the sub-tile's logits from K (still in LDS), takes their exact
+// maximum, rescales O and l and recomputes P. The row sums are of the
+// unrounded probabilities, so the log-sum-exp is the exact one.
 // Layout conventions (S^T = K Q^T, O^T = V^T P^T, V^T by transpose reads)
 // are those of attn_fwd_bf16.h. Built with -mllvm -amdgpu-mfma-vgpr-form.
 #pragma once
@@ -63,7 +64,7 @@ struct PipeCfg {
   static_assert(kKTile <= kSlot && kVTile <= kSlot, "tile fits its slot");
 };
 
-constexpr float kPipeSumLimit = 256.0f;    // 2^8
+constexpr float kPipeSumLimit = 0x1p64f;   // overflow guard: far below FLT_MAX / N
 
 // Key-range split of the last, partly filled round of workgroups. The first
 // n_full workgroups each take one 256-row query tile over all keys. The next
@@ -367,7 +368,7 @@ void attn_fwd_bf16_pipe_kernel(const uint16_t* __restrict__ Qg, const uint16_t* 
     // The packed P must exist here: without this the compiler sinks the bf16
     // packs past the rare-path branch, out of the MFMA phases.
     asm volatile("" ::"v"(pout[0][0]), "v"(pout[0][1]), "v"(pout[1][0]), "v"(pout[1][1]));
-    // ---- rare path: a probability of sub-tile j exceeded 2^8
+    // ---- rare path: a row sum of sub-tile j passed 2^64 or is not finite
     const bool bad = !(ls0 <= kPipeSumLimit) || !(ls1 <= kPipeSumLimit);
     if (__builtin_expect(__builtin_amdgcn_ballot_w64(bad) != 0, 0)) {
       read_kfrags(j);                      // K tiles j/2 and (j+2)/2 are still in their slots

@@ -13,13 +13,17 @@
 //   swizzle of attn_fwd_fp8.h, which the DMA applies by choosing each lane's
 //   source chunk; V^T fragments come from ds_read_b64_tr_b8 and P^T is packed
 //   from the S^T accumulators in the matching key order;
-// * probabilities are scaled by 8 before the e4m3 cast (the factor is added
-//   to the exponent argument), and the row sums use the unrounded fp32
-//   values. The e4m3 cast saturates above 448, i.e. for p > 56 relative to
-//   the running maximum; a row sum above 448 in some lane (which any such p
-//   implies, and which 32 probabilities of at most 1 cannot reach) sends the
-//   sub-tile down the rare path, which recomputes its logits from K in LDS,
-//   takes their exact maximum and rescales;
+// * probabilities are scaled by 2 before the e4m3 cast (the factor is added
+//   to the exponent argument): p down to 2^-8 of the running maximum stays
+//   in the normal e4m3 range, and p up to 232 times it fits (the maximum of
+//   the first sub-tile is usually a few bits below the row's). A power of
+//   two cancels in O. The row sums are those of the e4m3 values,
+//   taken on the matrix core (the output's denominator; the exact sums for
+//   the log-sum-exp are fp32 adds, only in the EXACT_LSE form). The cast does
+//   not saturate: past 464 (p > 232 relative to the running maximum) it gives
+//   the e4m3 NaN, which makes the half-row sum NaN; that sends the sub-tile
+//   down the rare path, which recomputes its logits from K in LDS, takes their
+//   exact maximum and rescales. Large but representable p take no detour;
 // * per-tensor descales dq, dk fold into the logit multiplier and dv into the
 //   epilogue.
 // Sub-iteration j (64 keys), two phases of 8 MFMAs each:
@@ -50,8 +54,7 @@ struct Fp8PipeCfg {
   static_assert(kKTile <= kSlot && kVTile <= kSlot, "tile fits its slot");
 };
 
-constexpr float kFp8PipeSumLimit = 448.0f;     // largest e4m3 value
-constexpr float kFp8PipePLog2 = 3.0f;          // P is scaled by 2^3 before the cast
+constexpr float kFp8PipePLog2 = 1.0f;          // P is scaled by 2 before the cast
 
 #define DIT_FENCE() __builtin_amdgcn_sched_barrier(0)
 
@@ -337,7 +340,7 @@ void attn_fwd_fp8_pipe_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __r
           smfma(s1[1], 1, 1, 0);
         } else {
           // ahead of the last S MFMA, so that the sums are ready when the
-          // saturation test reads them
+          // range test reads them
           rs1 = psum(pout[1]);
           DIT_FENCE();
           smfma(s1[1], 1, 1, 1);
@@ -360,14 +363,13 @@ void attn_fwd_fp8_pipe_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __r
     // The packed P must exist here: without this the compiler sinks the e4m3
     // conversions past the rare-path branch, out of the MFMA phases.
     asm volatile("" ::"v"(pout[0]), "v"(pout[1]));
-    // ---- rare path: some p reached the e4m3 range limit (a saturated 448, or
-    // a NaN, makes its half-row sum fail the test)
-    // The sums are >= +0 or NaN, so their bit patterns order like the values
-    // (a NaN above every finite one): an unsigned maximum needs no NaN care.
+    // ---- rare path: some p passed the e4m3 range (its NaN made a half-row
+    // sum NaN). The sums are >= +0 or NaN, so their bit patterns order like
+    // the values, with every NaN above +inf: one unsigned maximum decides.
     auto u = [](float x) { return __float_as_uint(x); };
     const uint32_t big = max(max(max(u(rs0[0]), u(rs0[1])), max(u(rs0[2]), u(rs0[3]))),
                              max(max(u(rs1[0]), u(rs1[1])), max(u(rs1[2]), u(rs1[3]))));
-    if (__builtin_amdgcn_ballot_w64(big >= u(kFp8PipeSumLimit)) != 0) {
+    if (__builtin_amdgcn_ballot_w64(big > 0x7F800000u) != 0) {
       // Recompute S_j from K in LDS into the registers of S_{j+1}, take its
       // exact row maxima, rescale, redo P_j; then recompute S_{j+1}. Reusing
       // those registers keeps this path's working set to one accumulator

@@ -149,3 +149,26 @@ def test_unsupported_head_dim_on_device():
     with pytest.raises(dit.DitAttnError) as e:
         dit.attention(x, x, x)
     assert e.value.status == dit.DIT_ATTN_EUNSUPPORTED
+
+
+def _ramp_qkv(N, d, slope, seed):
+    """Logits that grow along the keys: q = e_0, k_j = slope * j * e_0 (plus
+    small noise in the other coordinates), V random. The running maximum taken
+    from the first keys goes stale by slope * scale * N nats over the row."""
+    g = torch.Generator().manual_seed(seed)
+    q = torch.zeros((1, 2, N, d))
+    q[..., 0] = 1.0
+    k = 0.01 * torch.randn((1, 2, N, d), generator=g)
+    k[..., 0] = slope * torch.arange(N, dtype=torch.float32)
+    v = torch.randn((1, 2, N, d), generator=g)
+    return q.to(torch.bfloat16), k.to(torch.bfloat16), v.to(torch.bfloat16)
+
+
+@pytest.mark.parametrize("slope,label", [(17.5, "rare path every sub-tile"), (0.4, "large P, no rare path")])
+def test_growing_logits(slope, label):
+    """17.5: each 32-key sub-tile raises the maximum by more than 64 bits, so
+    every sub-tile takes the recompute path. 0.4: the maximum grows by about
+    50 bits over the row, below the 2^64 guard, so probabilities relative to
+    the first sub-tile's maximum reach about 2^50 and are used as they are."""
+    q, k, v = _ramp_qkv(1000, 128, slope, seed=31)
+    _full_check(q, k, v, 1 / math.sqrt(128), f"ramp slope {slope} ({label})")

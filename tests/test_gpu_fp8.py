@@ -12,7 +12,8 @@ Gates for the fp8 attention (bf16 output):
   the input quantisation, which dominates, is bit-identical.
   Gate: mean error <= 1.25 e_emul(mean) + 1e-5 and max error <= 2 e_emul(max).
 * the log-sum-exp is the exact one (sums of the unrounded p), against the
-  emulation's to 1e-4.
+  emulation's to 1e-4 + 1e-5|lse| plus the logit error of the e4m3 MFMA's
+  inexact internal sums (see _check_fp8).
 * O does not depend on whether the log-sum-exp is requested (two kernel
   forms): bitwise equal at the full workload.
 """
@@ -105,7 +106,18 @@ def _check_fp8(q, k, v, scale, label, rows=None, spec_gate=False):
         assert err.max() <= SPEC_MAX_FP8
     assert err.mean() <= 1.25 * err_e.mean() + 1e-5
     assert err.max() <= 2.0 * err_e.max() + 1e-5
-    assert np.allclose(lse[:, :, rows], lse_emul, rtol=1e-5, atol=1e-4)
+    # The 32x32x64 e4m3 MFMA does not sum its 64 products exactly: measured,
+    # a sum loses up to about 2^-11 of the sum of its terms' magnitudes (small
+    # terms beside a large one are truncated). The log-sum-exp moves by at most
+    # the largest logit error, so per row
+    #   |d lse_i| <= 2^-11 scale max_j sum_k |q_ik k_jk| <= 2^-11 scale |q_i| max_j |k_j|
+    # (Cauchy-Schwarz, dequantised values) on top of the fp32 terms.
+    qn = np.linalg.norm(oracle.e4m3_decode(q8[:, :, rows]) * np.float64(dq), axis=-1)
+    kn = np.linalg.norm(oracle.e4m3_decode(k8) * np.float64(dk), axis=-1).max(axis=-1, keepdims=True)
+    tol = 1e-4 + 1e-5 * np.abs(lse_emul) + 2.0**-11 * scale * qn * kn
+    d_lse = np.abs(lse[:, :, rows] - lse_emul)
+    say(f"  {label}: lse max |d| {d_lse.max():.3e} (largest allowed {tol.max():.3e}, smallest {tol.min():.3e})")
+    assert (d_lse <= tol).all(), (d_lse - tol).max()
 
 
 @pytest.mark.parametrize("N", [1, 65, 300, 1000])
@@ -114,11 +126,14 @@ def test_fp8_small(N):
     _check_fp8(q, k, v, 1 / math.sqrt(128), f"N={N}")
 
 
-def test_fp8_workload_sampled_rows():
-    w = WORKLOADS["t2i_2048_fp8"]
+@pytest.mark.parametrize("name", ["t2i_2048_fp8", "t2i_2048_peaked"])
+def test_fp8_workload_sampled_rows(name):
+    """The spec gate applies to the workload it is stated for; the peaked rows
+    (Q x 4) take the recompute path often and are held to the calibrated gate."""
+    w = WORKLOADS[name]
     q, k, v = make_qkv(w)
     rows = sample_rows(w.N, seed=0, n_edge=128, stride=64)
-    _check_fp8(q, k, v, 1 / math.sqrt(128), "t2i_2048_fp8", rows=rows, spec_gate=True)
+    _check_fp8(q, k, v, 1 / math.sqrt(128), name, rows=rows, spec_gate=name == "t2i_2048_fp8")
 
 
 def test_fp8_output_independent_of_lse_request():
@@ -130,6 +145,20 @@ def test_fp8_output_independent_of_lse_request():
         o1, _ = _run_fp8(q, k, v, 1 / math.sqrt(128), want_lse=True)
         o0, _ = _run_fp8(q, k, v, 1 / math.sqrt(128), want_lse=False)
         assert np.array_equal(o0, o1), (name, np.abs(o0 - o1).max())
+
+
+def test_fp8_growing_logits_rare_path():
+    """Logits that grow by about 10 bits per 64-key sub-tile: relative to the
+    stale running maximum the probabilities leave the e4m3 range (NaN), and
+    every sub-tile takes the recompute path."""
+    N, d = 1000, 128
+    g = torch.Generator().manual_seed(33)
+    q = torch.zeros((1, 2, N, d))
+    q[..., 0] = 1.0
+    k = 0.01 * torch.randn((1, 2, N, d), generator=g)
+    k[..., 0] = 1.25 * torch.arange(N, dtype=torch.float32)
+    v = torch.randn((1, 2, N, d), generator=g)
+    _check_fp8(q.to(torch.bfloat16), k.to(torch.bfloat16), v.to(torch.bfloat16), 1 / math.sqrt(d), "ramp")
 
 
 def test_fp8_tile_coverage_exact():
