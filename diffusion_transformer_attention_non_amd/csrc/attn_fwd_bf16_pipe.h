@@ -21,10 +21,11 @@
 //
 // Sub-iteration j (32 keys), two phases of 8 steps. Each step is one
 // O^T += V_{j-1}^T P_{j-1}^T MFMA and one S_{j+1} = K_{j+1} Q^T MFMA (a chain
-// over d), with half of a fixed VALU mix behind each MFMA: two exponentials
-// of P_j with their row-sum adds and one bf16 pack, and two FMAs forming
-// exponent arguments (of S_j's second query block in phase X, of S_{j+1}'s
-// first in phase Y). Fragment reads from LDS follow the MFMA that last reads
+// over d), with a fixed VALU mix split around the two MFMAs: two exponentials
+// of P_j and two FMAs forming exponent arguments (of S_j's second query block
+// in phase X, of S_{j+1}'s first in phase Y) behind the first, the row-sum
+// adds and the bf16 pack of those two exponentials behind the second, so that
+// no instruction waits on the transcendental unit's result. Fragment reads from LDS follow the MFMA that last reads
 // the register they fill: V_j over both phases, K_{j+2} over phase Y. P
 // alternates between two register sets over the two sub-iterations of a
 // tile, so nothing is copied at the loop edge. Row sums are fp32 adds: a
@@ -241,6 +242,12 @@ void attn_fwd_bf16_pipe_kernel(const uint16_t* __restrict__ Qg, const uint16_t* 
     asm volatile("" : "+v"(ls));       // keeps the add in this step
     return p;
   };
+  // exp2 now, its row-sum add later: the add waits on the transcendental unit
+  auto exp_raw = [&](const f32x16_t& t, int i) __attribute__((always_inline)) {
+    float p = fast_exp2(t[i]);
+    asm volatile("" : "+v"(p));
+    return p;
+  };
   auto pack_word = [&](float a, float b, int e, bf16x8_t (&out)[2]) __attribute__((always_inline)) {
     const bf16x2_t pk = {(__bf16)a, (__bf16)b};
     int word = __builtin_bit_cast(int, pk);
@@ -248,6 +255,14 @@ void attn_fwd_bf16_pipe_kernel(const uint16_t* __restrict__ Qg, const uint16_t* 
     i32x4_t w = __builtin_bit_cast(i32x4_t, out[e >> 2]);
     w[e & 3] = word;
     out[e >> 2] = __builtin_bit_cast(bf16x8_t, w);
+  };
+  // the row-sum adds and the pack of two p, placed at this point
+  auto sum_pack = [&](float& ls, float a, float b, int e, bf16x8_t (&out)[2]) __attribute__((always_inline)) {
+    asm volatile("" : "+v"(a), "+v"(b));
+    ls += a;
+    ls += b;
+    asm volatile("" : "+v"(ls));
+    pack_word(a, b, e, out);
   };
 
   f32x16_t acc[2][DB];
@@ -319,9 +334,9 @@ void attn_fwd_bf16_pipe_kernel(const uint16_t* __restrict__ Qg, const uint16_t* 
       for (int st = 0; st < 8; ++st) {
         const int qb = st & 1, db = st >> 1;
         acc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[0][db], pin[qb][0], acc[qb][db], 0, 0, 0);
+        const float pa = exp_raw(t0, 2 * st), pb = exp_raw(t0, 2 * st + 1);
         t1[2 * st] = fmaf(s1[2 * st], scale_log2, -m1);
         t1[2 * st + 1] = fmaf(s1[2 * st + 1], scale_log2, -m1);
-        const float pa = exp_one(t0, 2 * st, ls0);
         if ((st & 1) == 0) dma(st >> 1);
         DIT_FENCE();
         if (st == 0) {
@@ -329,8 +344,7 @@ void attn_fwd_bf16_pipe_kernel(const uint16_t* __restrict__ Qg, const uint16_t* 
           for (int r = 0; r < 16; ++r) sa[r] = 0.f;
         }
         sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[st], qf[0][st], sa, 0, 0, 0);
-        const float pb = exp_one(t0, 2 * st + 1, ls0);
-        pack_word(pa, pb, st, pout[0]);
+        sum_pack(ls0, pa, pb, st, pout[0]);
         if (st & 1) read_vfrag(vb, 0, db);      // both query blocks have used vf[0][db]
         DIT_FENCE();
       }
@@ -345,17 +359,16 @@ void attn_fwd_bf16_pipe_kernel(const uint16_t* __restrict__ Qg, const uint16_t* 
       for (int st = 0; st < 8; ++st) {
         const int qb = st & 1, db = st >> 1;
         acc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[1][db], pin[qb][1], acc[qb][db], 0, 0, 0);
+        const float pa = exp_raw(t1, 2 * st), pb = exp_raw(t1, 2 * st + 1);
         t0[2 * st] = fmaf(sa[2 * st], scale_log2, -m0);        // S_{j+1}'s arguments
         t0[2 * st + 1] = fmaf(sa[2 * st + 1], scale_log2, -m0);
-        const float pa = exp_one(t1, 2 * st, ls1);
         DIT_FENCE();
         if (st == 0) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) sb[r] = 0.f;
         }
         sb = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[st], qf[1][st], sb, 0, 0, 0);
-        const float pb = exp_one(t1, 2 * st + 1, ls1);
-        pack_word(pa, pb, st, pout[1]);
+        sum_pack(ls1, pa, pb, st, pout[1]);
         read_kfrag(kb2, st);                     // kf[st] is free: K_{j+2}
         if (st & 1) read_vfrag(vb, 1, db);
         DIT_FENCE();
