@@ -28,7 +28,7 @@ sys.path.insert(0, ROOT)
 METRIC = "DiT attention fwd TFLOP/s at 16896-token shape; % of MI355X MFMA peak"
 PEAK_TFLOPS = {"bf16": 2516.6, "fp8": 5033.2}     # MI355X dense MFMA, 2.4 GHz
 HBM_PEAK_GBS = 8000.0
-KERNEL_SOURCES = ["attn_common.h", "attn_fwd_bf16.h", "attn_fwd_bf16_pipe.h", "attn_fwd_fp8.h", "attn_fwd_fp8_pipe.h", "dit_attn.hip"]
+KERNEL_SOURCES = ["attn_common.h", "attn_fwd_bf16.h", "attn_fwd_bf16_pipe.h", "attn_fwd_fp8_pipe.h", "dit_attn.hip"]
 
 
 def kernel_source_hash() -> str:
@@ -111,6 +111,9 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="t2i_2048")
     ap.add_argument("--no-fp8", action="store_true", help="skip the fp8-e4m3 companion measurement")
+    ap.add_argument("--layout", choices=["bhnd", "bnhd"], default="bhnd",
+                    help="rows of q, k, v and o packed as [B][H][N][d] (default) or taken from [B][N][H][d] "
+                         "buffers through dit_attn_fwd_strided")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -141,14 +144,24 @@ def main(argv=None):
     scale = 1.0 / math.sqrt(w.d)
     dev = torch.device("cuda:0")
     q, k, v = make_qkv(w)
-    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
-    od = torch.empty_like(qd)
+    B, H, N, d = w.B, w.H, w.N, w.d
+    if args.layout == "bnhd":
+        # (B, H, N, d) views of (B, N, H, d) buffers, as a QKV projection writes them
+        qd, kd, vd = (t.permute(0, 2, 1, 3).contiguous().to(dev).permute(0, 2, 1, 3) for t in (q, k, v))
+        od = torch.empty((B, N, H, d), dtype=torch.bfloat16, device=dev).permute(0, 2, 1, 3)
+    else:
+        qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+        od = torch.empty_like(qd)
     stream = torch.cuda.current_stream()
     handle = stream.cuda_stream
-    B, H, N, d = w.B, w.H, w.N, w.d
+    in_strides, out_strides = qd.stride()[:3], od.stride()[:3]
 
     def step():
-        st = dit.dit_attn_fwd(qd, kd, vd, od, B, H, N, d, scale, dit.DIT_ATTN_BF16, handle)
+        if args.layout == "bnhd":
+            st = dit.dit_attn_fwd_strided(qd, kd, vd, od, B, H, N, d, scale, dit.DIT_ATTN_BF16, in_strides,
+                                          out_strides, None, None, handle)
+        else:
+            st = dit.dit_attn_fwd(qd, kd, vd, od, B, H, N, d, scale, dit.DIT_ATTN_BF16, handle)
         if st != 0:
             raise dit.DitAttnError(st, "dit_attn_fwd")
 
@@ -166,7 +179,7 @@ def main(argv=None):
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic: Q, K, V iid N(0,1) rounded to bf16, seed 0",
         "config": {"workload": w.name, "B": B, "H": H, "N": N, "d": d, "n_text": w.n_text,
-                   "n_image": w.n_image, "causal": False, "scale": scale},
+                   "n_image": w.n_image, "causal": False, "scale": scale, "layout": args.layout},
         "pct_of_peak": round(100.0 * value / peak, 2),
         "kernel_ms": {"mean": round(k_mean, 4), "median": round(statistics.median(per), 4),
                       "p95": round(sorted(per)[int(0.95 * (len(per) - 1))], 4), "min": round(min(per), 4)},
@@ -175,16 +188,19 @@ def main(argv=None):
     }
 
     if not args.no_fp8:
-        q8, dsq = dit.quantize_e4m3(qd)
-        k8, dsk = dit.quantize_e4m3(kd)
-        v8, dsv = dit.quantize_e4m3(vd)
-        descale = torch.cat([dsq, dsk, dsv]).contiguous()
+        if args.layout == "bnhd":      # quantise the (B, N, H, d) buffers, view them as (B, H, N, d)
+            quant = [dit.quantize_e4m3(t.permute(0, 2, 1, 3)) for t in (qd, kd, vd)]
+            q8, k8, v8 = (c.permute(0, 2, 1, 3) for c, _ in quant)
+        else:
+            quant = [dit.quantize_e4m3(t) for t in (qd, kd, vd)]
+            q8, k8, v8 = (c for c, _ in quant)
+        descale = torch.cat([ds for _, ds in quant]).contiguous()
 
         def step8():
-            st = dit.dit_attn_fwd_ex(q8, k8, v8, od, B, H, N, d, scale, dit.DIT_ATTN_FP8_E4M3, descale, None,
-                                     handle)
+            st = dit.dit_attn_fwd_strided(q8, k8, v8, od, B, H, N, d, scale, dit.DIT_ATTN_FP8_E4M3,
+                                          q8.stride()[:3], out_strides, descale, None, handle)
             if st != 0:
-                raise dit.DitAttnError(st, "dit_attn_fwd_ex")
+                raise dit.DitAttnError(st, "dit_attn_fwd_strided")
 
         wall8, per8 = time_launches(step8, args.warmup, args.steps)
         v8_tflops = flops / (wall8 / args.steps) / 1e12

@@ -12,11 +12,12 @@ import math
 
 from . import _lib
 from ._lib import (DIT_ATTN_BF16, DIT_ATTN_EDEVICE, DIT_ATTN_EINVAL, DIT_ATTN_ELAUNCH, DIT_ATTN_FP8_E4M3,
-                   DIT_ATTN_OK, DIT_ATTN_EUNSUPPORTED, dit_attn_fwd, dit_attn_fwd_ex, dit_attn_quantize_e4m3,
-                   dit_attn_strerror, dit_attn_version)
+                   DIT_ATTN_OK, DIT_ATTN_EUNSUPPORTED, dit_attn_fwd, dit_attn_fwd_ex, dit_attn_fwd_strided,
+                   dit_attn_quantize_e4m3, dit_attn_strerror, dit_attn_version)
 
 __all__ = [
-    "DitAttnError", "attention", "quantize_e4m3", "dit_attn_fwd", "dit_attn_fwd_ex", "dit_attn_quantize_e4m3",
+    "DitAttnError", "attention", "quantize_e4m3", "dit_attn_fwd", "dit_attn_fwd_ex", "dit_attn_fwd_strided",
+    "dit_attn_quantize_e4m3",
     "dit_attn_strerror", "dit_attn_version", "DIT_ATTN_BF16", "DIT_ATTN_FP8_E4M3", "DIT_ATTN_OK",
     "DIT_ATTN_EINVAL", "DIT_ATTN_EUNSUPPORTED", "DIT_ATTN_EDEVICE", "DIT_ATTN_ELAUNCH",
 ]
@@ -38,10 +39,13 @@ def attention(q, k, v, scale: float | None = None, *, out=None, lse=None, descal
     """Dense non-causal attention of (B, H, N, d) device tensors.
 
     bf16 inputs (d in {64, 128}) or float8_e4m3fn inputs (d = 128, with an
-    optional device float32 ``descale`` tensor [dq, dk, dv]). Returns the bf16
-    output; writes the natural-log row normaliser into ``lse`` (float32
-    (B, H, N)) when given. Runs on ``stream`` (default: torch's current
-    stream) without synchronising."""
+    optional device float32 ``descale`` tensor [dq, dk, dv]). q, k and v may
+    be strided views (e.g. of a (B, N, H, d) or (B, N, 3, H, d) buffer, seen
+    as (B, H, N, d)) as long as d is contiguous and the three share strides;
+    ``out`` (default: a new contiguous bf16 tensor) may be strided the same
+    way. Returns the bf16 output; writes the natural-log row normaliser into
+    ``lse`` (float32 (B, H, N), contiguous) when given. Runs on ``stream``
+    (default: torch's current stream) without synchronising."""
     import torch
     if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape:
         raise ValueError("q, k, v must share one (B, H, N, d) shape")
@@ -54,22 +58,25 @@ def attention(q, k, v, scale: float | None = None, *, out=None, lse=None, descal
     else:
         raise ValueError(f"unsupported dtype {q.dtype}")
     for t in (q, k, v):
-        if not t.is_cuda or not t.is_contiguous():
-            raise ValueError("q, k, v must be contiguous device tensors")
+        if not t.is_cuda or t.stride(3) != 1:
+            raise ValueError("q, k, v must be device tensors with a contiguous last dimension")
+    if k.stride() != q.stride() or v.stride() != q.stride():
+        raise ValueError("q, k, v must share strides")
     B, H, N, d = q.shape
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if out is None:
         out = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=q.device)
-    elif out.shape != q.shape or out.dtype != torch.bfloat16 or not out.is_contiguous():
-        raise ValueError("out must be a contiguous bf16 tensor of q's shape")
+    elif out.shape != q.shape or out.dtype != torch.bfloat16 or not out.is_cuda or out.stride(3) != 1:
+        raise ValueError("out must be a bf16 device tensor of q's shape with a contiguous last dimension")
     if lse is not None and (lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous()):
         raise ValueError("lse must be a contiguous float32 (B, H, N) tensor")
     if descale is not None and (descale.numel() != 3 or descale.dtype != torch.float32 or not descale.is_cuda):
         raise ValueError("descale must be a float32 device tensor of 3 elements")
-    st = dit_attn_fwd_ex(q, k, v, out, B, H, N, d, float(scale), dtype, descale, lse, _stream_handle(stream))
+    st = dit_attn_fwd_strided(q, k, v, out, B, H, N, d, float(scale), dtype, q.stride()[:3], out.stride()[:3],
+                              descale, lse, _stream_handle(stream))
     if st != DIT_ATTN_OK:
-        raise DitAttnError(st, "dit_attn_fwd_ex")
+        raise DitAttnError(st, "dit_attn_fwd_strided")
     return out
 
 

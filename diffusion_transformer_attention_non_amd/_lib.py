@@ -19,8 +19,8 @@ DIT_ATTN_EUNSUPPORTED = -2
 DIT_ATTN_EDEVICE = -3
 DIT_ATTN_ELAUNCH = -4
 
-EXPORTED = ("dit_attn_fwd", "dit_attn_fwd_ex", "dit_attn_quantize_e4m3", "dit_attn_strerror",
-            "dit_attn_version")
+EXPORTED = ("dit_attn_fwd", "dit_attn_fwd_ex", "dit_attn_fwd_strided", "dit_attn_quantize_e4m3",
+            "dit_attn_strerror", "dit_attn_version")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is not built; run `python -m diffusion_transformer_attention_non_amd.build` "
@@ -32,6 +32,8 @@ _lib.dit_attn_fwd.argtypes = [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _vp]
 _lib.dit_attn_fwd.restype = _i
 _lib.dit_attn_fwd_ex.argtypes = [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _vp, _vp, _vp]
 _lib.dit_attn_fwd_ex.restype = _i
+_lib.dit_attn_fwd_strided.argtypes = [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _vp, _vp, _vp, _vp, _vp]
+_lib.dit_attn_fwd_strided.restype = _i
 _lib.dit_attn_quantize_e4m3.argtypes = [_vp, _i64, _vp, _vp, _vp, _vp]
 _lib.dit_attn_quantize_e4m3.restype = _i
 _lib.dit_attn_strerror.argtypes = [_i]
@@ -56,6 +58,20 @@ def dit_attn_fwd(q, k, v, o, B, H, N, d, scale, dtype, stream=None) -> int:
 def dit_attn_fwd_ex(q, k, v, o, B, H, N, d, scale, dtype, descale_qkv=None, lse=None, stream=None) -> int:
     return _lib.dit_attn_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, H, N, d, scale, dtype,
                                 _ptr(descale_qkv), _ptr(lse), _ptr(stream))
+
+
+def dit_attn_fwd_strided(q, k, v, o, B, H, N, d, scale, dtype, qkv_strides=None, o_strides=None,
+                         descale_qkv=None, lse=None, stream=None) -> int:
+    qs, os_ = (ctypes.c_int64 * 3)(), (ctypes.c_int64 * 3)()
+    qp = op = None
+    if qkv_strides is not None:
+        qs[:] = [int(x) for x in qkv_strides]
+        qp = ctypes.cast(qs, ctypes.c_void_p)
+    if o_strides is not None:
+        os_[:] = [int(x) for x in o_strides]
+        op = ctypes.cast(os_, ctypes.c_void_p)
+    return _lib.dit_attn_fwd_strided(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, H, N, d, scale, dtype, qp, op,
+                                     _ptr(descale_qkv), _ptr(lse), _ptr(stream))
 
 
 def dit_attn_quantize_e4m3(x, n, x8, descale, amax_ws, stream=None) -> int:

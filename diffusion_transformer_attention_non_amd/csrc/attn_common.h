@@ -17,6 +17,23 @@ typedef short i16x4_t __attribute__((ext_vector_type(4)));
 
 #define DIT_LDS(T, p) ((__attribute__((address_space(3))) T*)(p))
 
+// Where the rows of one (b, h) live: element strides of batch, head and token
+// for q, k, v (shared) and for o. The d values of a row are contiguous.
+// Contiguous [B][H][N][d]: qb = H N d, qh = N d, qn = d (and the same for o).
+struct Layout {
+  long long qb, qh, qn;
+  long long ob, oh, on;
+  int H;
+  __device__ __forceinline__ long long in_off(int bh) const {
+    const int b = bh / H;
+    return (long long)b * qb + (long long)(bh - b * H) * qh;
+  }
+  __device__ __forceinline__ long long out_off(int bh) const {
+    const int b = bh / H;
+    return (long long)b * ob + (long long)(bh - b * H) * oh;
+  }
+};
+
 // Workgroups are dispatched round-robin over the 8 XCDs (blockIdx % 8), and
 // each XCD has its own L2. Remap so that each XCD receives one contiguous
 // range of logical tiles: consecutive q-tiles of one head then share their

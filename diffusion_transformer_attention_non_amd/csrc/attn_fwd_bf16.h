@@ -78,7 +78,7 @@ __global__ __launch_bounds__(C::kThreads)
 void attn_fwd_bf16_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
                           const uint16_t* __restrict__ Vg, uint16_t* __restrict__ Og,
                           float* __restrict__ LSEg, int N, int n_qtiles,
-                          float scale_log2, float scale) {
+                          float scale_log2, float scale, Layout L) {
   constexpr int D = C::kD, QB = C::kQB, KB = C::kKB, KS = C::kKS, DB = C::kDB, KBLK = C::kKBLK;
   constexpr int CH = C::kChunks, TB = C::kTileBytes;
   extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -86,10 +86,10 @@ void attn_fwd_bf16_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __res
   const int tile = xcd_remap(blockIdx.x, gridDim.x);
   const int bh = tile / n_qtiles;
   const int qt = tile - bh * n_qtiles;
-  const size_t base = (size_t)bh * (size_t)N * D;
-  const uint16_t* Q = Qg + base;
-  const uint16_t* K = Kg + base;
-  const uint16_t* V = Vg + base;
+  const long long ibase = L.in_off(bh);
+  const uint16_t* Q = Qg + ibase;
+  const uint16_t* K = Kg + ibase;
+  const uint16_t* V = Vg + ibase;
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
@@ -104,7 +104,7 @@ void attn_fwd_bf16_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __res
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       i32x4_t raw = {0, 0, 0, 0};
-      if (row < N) raw = *(const i32x4_t*)(Q + (size_t)row * D + ks * 16 + hh * 8);
+      if (row < N) raw = *(const i32x4_t*)(Q + (long long)row * L.qn + ks * 16 + hh * 8);
       qf[qb][ks] = __builtin_bit_cast(bf16x8_t, raw);
     }
   }
@@ -131,8 +131,8 @@ void attn_fwd_bf16_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __res
       const int r = ci / CH, c = ci % CH;
       const int key = kt * KB + r;
       if (key < N) {
-        stK[i] = *(const i32x4_t*)(K + (size_t)key * D + c * 8);
-        stV[i] = *(const i32x4_t*)(V + (size_t)key * D + c * 8);
+        stK[i] = *(const i32x4_t*)(K + (long long)key * L.qn + c * 8);
+        stV[i] = *(const i32x4_t*)(V + (long long)key * L.qn + c * 8);
       } else {
         stK[i] = i32x4_t{0, 0, 0, 0};
         stV[i] = i32x4_t{0, 0, 0, 0};
@@ -283,7 +283,7 @@ void attn_fwd_bf16_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __res
     const float inv = 1.0f / l_tot;
     const int row = q0 + qb * 32 + l32;
     if (row < N) {
-      uint16_t* orow = Og + base + (size_t)row * D;
+      uint16_t* orow = Og + L.out_off(bh) + (long long)row * L.on;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll

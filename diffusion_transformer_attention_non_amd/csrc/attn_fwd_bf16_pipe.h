@@ -98,7 +98,7 @@ __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(1, 
 void attn_fwd_bf16_pipe_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
                                const uint16_t* __restrict__ Vg, uint16_t* __restrict__ Og,
                                float* __restrict__ LSEg, int N, int n_qtiles, float scale_log2, float scale,
-                               PipeSplit split) {
+                               PipeSplit split, Layout L) {
   constexpr int D = C::kD, KS = C::kKS, DB = C::kDB;
   constexpr int KROW = C::kKRow, VROW = C::kVRow;
   extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -120,9 +120,10 @@ void attn_fwd_bf16_pipe_kernel(const uint16_t* __restrict__ Qg, const uint16_t* 
   }
   const int bh = tile / n_qtiles;
   const int qt = tile - bh * n_qtiles;
-  const size_t base = (size_t)bh * (size_t)N * D;
-  const char* Kh = reinterpret_cast<const char*>(Kg + base);
-  const char* Vh = reinterpret_cast<const char*>(Vg + base);
+  const long long ibase = L.in_off(bh), obase = L.out_off(bh);
+  const int rowb = (int)(L.qn * 2);       // bytes between consecutive tokens of q, k, v
+  const char* Kh = reinterpret_cast<const char*>(Kg + ibase);
+  const char* Vh = reinterpret_cast<const char*>(Vg + ibase);
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -133,12 +134,12 @@ void attn_fwd_bf16_pipe_kernel(const uint16_t* __restrict__ Qg, const uint16_t* 
   bf16x8_t qf[2][KS];
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
-    const uint16_t* Q = Qg + base;
+    const uint16_t* Q = Qg + ibase;
     const int row = q0 + qb * 32 + l32;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       i32x4_t raw = {0, 0, 0, 0};
-      if (row < N) raw = *(const i32x4_t*)(Q + (size_t)row * D + ks * 16 + hh * 8);
+      if (row < N) raw = *(const i32x4_t*)(Q + (long long)row * L.qn + ks * 16 + hh * 8);
       qf[qb][ks] = __builtin_bit_cast(bf16x8_t, raw);
     }
   }
@@ -153,17 +154,17 @@ void attn_fwd_bf16_pipe_kernel(const uint16_t* __restrict__ Qg, const uint16_t* 
     const int vr = s / (VROW / 16), vc = s % (VROW / 16);
     // padding slots get an offset past any tile (64 rows), so the range check
     // zero-fills them without a memory access
-    kdo[m] = kc < D / 8 ? kr * D * 2 + kc * 16 : 64 * D * 2;
-    vdo[m] = vc < D / 8 ? vr * D * 2 + vc * 16 : 64 * D * 2;
+    kdo[m] = kc < D / 8 ? kr * rowb + kc * 16 : 64 * rowb;
+    vdo[m] = vc < D / 8 ? vr * rowb + vc * 16 : 64 * rowb;
   }
   // buffer descriptor of one 64-key tile: the range check zero-fills rows past N
   auto tile_rsrc = [&](const char* head, int t) __attribute__((always_inline)) {
     const int rows = min(64, N - t * 64);
-    const unsigned long long a = (unsigned long long)(head + (size_t)t * 64 * D * 2);
+    const unsigned long long a = (unsigned long long)(head + (long long)t * 64 * rowb);
     i32x4_t rs;
     rs[0] = __builtin_amdgcn_readfirstlane((int)(unsigned)a);
     rs[1] = __builtin_amdgcn_readfirstlane((int)((a >> 32) & 0xffffu));   // stride 0
-    rs[2] = __builtin_amdgcn_readfirstlane(rows * D * 2);                   // bytes in range
+    rs[2] = __builtin_amdgcn_readfirstlane(rows * rowb);                    // bytes in range
     rs[3] = 0x00020000;
     return rs;
   };
@@ -499,7 +500,7 @@ void attn_fwd_bf16_pipe_kernel(const uint16_t* __restrict__ Qg, const uint16_t* 
     const float inv = 1.0f / l_tot;
     const int row = q0 + qb * 32 + l32;
     if (row < N) {
-      uint16_t* orow = Og + base + (size_t)row * D;
+      uint16_t* orow = Og + obase + (long long)row * L.on;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -524,7 +525,7 @@ void attn_fwd_bf16_pipe_kernel(const uint16_t* __restrict__ Qg, const uint16_t* 
 __global__ __launch_bounds__(256) void attn_split_combine_kernel(const float* __restrict__ ws_o,
                                                                  const float* __restrict__ ws_lse,
                                                                  uint16_t* __restrict__ Og, float* __restrict__ LSEg,
-                                                                 int N, int n_qtiles, PipeSplit split) {
+                                                                 int N, int n_qtiles, PipeSplit split, Layout L) {
   constexpr int D = PipeCfg::kD, BR = PipeCfg::kBR;
   const int ti = blockIdx.x / (BR / 8);
   const int r = (blockIdx.x % (BR / 8)) * 8 + (threadIdx.x >> 5);
@@ -556,7 +557,7 @@ __global__ __launch_bounds__(256) void attn_split_combine_kernel(const float* __
   uint2 out;
   out.x = pack_bf16x2(o[0] * inv, o[1] * inv);
   out.y = pack_bf16x2(o[2] * inv, o[3] * inv);
-  *(uint2*)(Og + ((size_t)bh * N + row) * D + c) = out;
+  *(uint2*)(Og + L.out_off(bh) + (long long)row * L.on + c) = out;
   if (LSEg != nullptr && c == 0)
     LSEg[(size_t)bh * N + row] =
         (split.ws_lse_out != nullptr ? lse_mx + __log2f(lse_sum) : mx + __log2f(wsum)) * 0.6931471805599453f;

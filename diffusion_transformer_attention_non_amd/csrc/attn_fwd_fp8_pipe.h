@@ -9,10 +9,15 @@
 // * both products run on the 32x32x64 f8f6f4 MFMA in its e4m3 x e4m3 form, so
 //   a sub-tile is 64 keys (the k extent of the PV product) and an LDS tile 128;
 // * K rows are 128 bytes padded to 144 (conflict-free ds_read_b128, additive
-//   addresses); V rows keep 128 bytes with the transpose-read-aware XOR
-//   swizzle of attn_fwd_fp8.h, which the DMA applies by choosing each lane's
-//   source chunk; V^T fragments come from ds_read_b64_tr_b8 and P^T is packed
-//   from the S^T accumulators in the matching key order;
+//   addresses); V rows keep 128 bytes with a transpose-read-aware XOR swizzle,
+//   which the DMA applies by choosing each lane's source chunk. LDS serves
+//   256 bytes (64 four-byte banks) per pass, so two 128-byte rows share a
+//   pass; a ds_read_b64_tr_b8 pass covers rows {0-3, 8-11} (+4) and two
+//   neighbouring 16-byte chunks c, c+1 (c even), and the 4 rows of each
+//   parity need {c ^ f, c ^ f ^ 1} disjoint: chunk c of row r is stored at
+//   c ^ f(r), f(r) = 2 ((r >> 1) & 1) + 4 ((r >> 3) & 1). V^T fragments come
+//   from ds_read_b64_tr_b8 and P^T is packed from the S^T accumulators in the
+//   matching key order;
 // * probabilities are scaled by 2 before the e4m3 cast (the factor is added
 //   to the exponent argument): p down to 2^-8 of the running maximum stays
 //   in the normal e4m3 range, and p up to 232 times it fits (the maximum of
@@ -35,7 +40,6 @@
 #pragma once
 #include "attn_common.h"
 #include "attn_fwd_bf16_pipe.h"   // dma_b128, flag_t, PipeSplit
-#include "attn_fwd_fp8.h"         // swz8_v, pack_e4m3x4
 
 namespace ditattn {
 
@@ -78,7 +82,7 @@ __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(1, 
 void attn_fwd_fp8_pipe_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __restrict__ Kg,
                               const uint8_t* __restrict__ Vg, uint16_t* __restrict__ Og,
                               float* __restrict__ LSEg, const float* __restrict__ descale,
-                              int N, int n_qtiles, float scale_log2, float scale, PipeSplit split) {
+                              int N, int n_qtiles, float scale_log2, float scale, PipeSplit split, Layout L) {
   constexpr int D = C::kD, KROW = C::kKRow;
   extern __shared__ __attribute__((aligned(16))) char smem[];
 
@@ -101,9 +105,10 @@ void attn_fwd_fp8_pipe_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __r
   }
   const int bh = tile / n_qtiles;
   const int qt = tile - bh * n_qtiles;
-  const size_t base = (size_t)bh * (size_t)N * D;
-  const char* Kh = reinterpret_cast<const char*>(Kg + base);
-  const char* Vh = reinterpret_cast<const char*>(Vg + base);
+  const long long ibase = L.in_off(bh), obase = L.out_off(bh);
+  const int rowb = (int)L.qn;             // bytes between consecutive tokens of q, k, v
+  const char* Kh = reinterpret_cast<const char*>(Kg + ibase);
+  const char* Vh = reinterpret_cast<const char*>(Vg + ibase);
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -120,7 +125,7 @@ void attn_fwd_fp8_pipe_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __r
     for (int ks = 0; ks < 2; ++ks) {
       i32x4_t a = {0, 0, 0, 0}, b = {0, 0, 0, 0};
       if (row < N) {
-        const uint8_t* p = Qg + base + (size_t)row * D + ks * 64 + hh * 32;
+        const uint8_t* p = Qg + ibase + (long long)row * L.qn + ks * 64 + hh * 32;
         a = *(const i32x4_t*)p;
         b = *(const i32x4_t*)(p + 16);
       }
@@ -135,18 +140,18 @@ void attn_fwd_fp8_pipe_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __r
   for (int m = 0; m < C::kDmaPerWave; ++m) {
     const int s = 64 * (wave + 4 * m) + lane;
     const int kr = s / (KROW / 16), kc = s % (KROW / 16);
-    kdo[m] = (kc < 8 && kr < C::kTileKeys) ? kr * D + kc * 16 : C::kTileKeys * D;   // past the tile: zeros
+    kdo[m] = (kc < 8 && kr < C::kTileKeys) ? kr * rowb + kc * 16 : C::kTileKeys * rowb;   // past the tile: zeros
     const int vr = s >> 3, vs = s & 7;
-    const int vc = vs ^ ((((vr >> 1) & 1) << 1) | (((vr >> 3) & 1) << 2));    // inverse of swz8_v
-    vdo[m] = vr < C::kTileKeys ? vr * D + vc * 16 : C::kTileKeys * D;
+    const int vc = vs ^ ((((vr >> 1) & 1) << 1) | (((vr >> 3) & 1) << 2));    // f(vr) is its own inverse
+    vdo[m] = vr < C::kTileKeys ? vr * rowb + vc * 16 : C::kTileKeys * rowb;
   }
   auto tile_rsrc = [&](const char* head, int t) __attribute__((always_inline)) {
     const int rows = min(C::kTileKeys, N - t * C::kTileKeys);
-    const unsigned long long a = (unsigned long long)(head + (size_t)t * C::kTileKeys * D);
+    const unsigned long long a = (unsigned long long)(head + (long long)t * C::kTileKeys * rowb);
     i32x4_t rs;
     rs[0] = __builtin_amdgcn_readfirstlane((int)(unsigned)a);
     rs[1] = __builtin_amdgcn_readfirstlane((int)((a >> 32) & 0xffffu));
-    rs[2] = __builtin_amdgcn_readfirstlane(rows * D);
+    rs[2] = __builtin_amdgcn_readfirstlane(rows * rowb);
     rs[3] = 0x00020000;
     return rs;
   };
@@ -504,7 +509,7 @@ void attn_fwd_fp8_pipe_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __r
     const float l_exact = EXACT_LSE ? pair_sum(l_ex[qb]) : 0.f;
     const int row = q0 + qb * 32 + l32;
     if (row < N) {
-      uint16_t* orow = Og + base + (size_t)row * D;
+      uint16_t* orow = Og + obase + (long long)row * L.on;
 #pragma unroll
       for (int db = 0; db < 4; ++db)
 #pragma unroll

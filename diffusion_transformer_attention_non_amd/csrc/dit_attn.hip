@@ -11,7 +11,6 @@
 #include "dit_attn.h"
 #include "attn_fwd_bf16.h"
 #include "attn_fwd_bf16_pipe.h"
-#include "attn_fwd_fp8.h"
 #include "attn_fwd_fp8_pipe.h"
 #include "quant_e4m3.h"
 
@@ -88,9 +87,40 @@ bool overlap(const void* a, uint64_t na, const void* b, uint64_t nb) {
   return pa < pb + nb && pb < pa + na;
 }
 
+// Checks one tensor's (batch, head, token) element strides and returns the
+// byte span its rows cover from the base pointer. Rows are d contiguous
+// elements; every row start must stay 16-byte aligned; a token stride below d
+// would overlap rows. For an output the map (b, h, n) -> row must be one to
+// one: taken by increasing stride, each dimension of size > 1 must step past
+// everything the smaller ones cover. Inputs may repeat rows (stride 0 shares
+// one head's K and V among heads).
+bool check_strides(const int64_t* s, int B, int H, int N, int d, unsigned esize, bool output, uint64_t* span) {
+  for (int i = 0; i < 3; ++i)
+    if (s[i] < 0 || s[i] > ((int64_t)1 << 40) || (s[i] * (int64_t)esize) % 16 != 0) return false;
+  if (s[2] < d) return false;
+  const unsigned __int128 last = (unsigned __int128)(B - 1) * (uint64_t)s[0] + (unsigned __int128)(H - 1) * (uint64_t)s[1] +
+                                 (unsigned __int128)(N - 1) * (uint64_t)s[2] + (unsigned)d;
+  if (last * esize >= ((unsigned __int128)1 << 62)) return false;
+  *span = (uint64_t)(last * esize);
+  if (output) {
+    int64_t st[3] = {s[0], s[1], s[2]};
+    int64_t sz[3] = {B, H, N};
+    for (int i = 0; i < 3; ++i)          // sort by stride
+      for (int j = i + 1; j < 3; ++j)
+        if (st[j] < st[i]) { std::swap(st[i], st[j]); std::swap(sz[i], sz[j]); }
+    unsigned __int128 cover = (unsigned)d;
+    for (int i = 0; i < 3; ++i) {
+      if (sz[i] == 1) continue;
+      if ((unsigned __int128)st[i] < cover) return false;
+      cover = (unsigned __int128)st[i] * (uint64_t)(sz[i] - 1) + cover;
+    }
+  }
+  return true;
+}
+
 template <class C>
 int launch_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int BH, int N,
-                float scale, hipStream_t st) {
+                float scale, hipStream_t st, const Layout& L) {
   const int n_qtiles = (N + C::kBR - 1) / C::kBR;
   const long long grid = (long long)n_qtiles * BH;
   if (grid > 0x7fffffffLL) return DIT_ATTN_EINVAL;
@@ -98,7 +128,7 @@ int launch_bf16(const void* q, const void* k, const void* v, void* o, float* lse
   hipLaunchKernelGGL(attn_fwd_bf16_kernel<C>, dim3((unsigned)grid), dim3(C::kThreads), C::kLdsBytes, st,
                      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                      static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), lse, N, n_qtiles,
-                     scale_log2, scale);
+                     scale_log2, scale, L);
   return hipGetLastError() == hipSuccess ? DIT_ATTN_OK : DIT_ATTN_ELAUNCH;
 }
 
@@ -137,7 +167,7 @@ int plan_split(int BH, int n_qtiles, int N, int key_tile, int n_cu, PipeSplit* s
 
 template <class C>
 int launch_pipe(const void* q, const void* k, const void* v, void* o, float* lse, int BH, int N,
-                float scale, hipStream_t st, int n_cu) {
+                float scale, hipStream_t st, int n_cu, const Layout& L) {
   const int n_qtiles = (N + C::kBR - 1) / C::kBR;
   const long long tiles = (long long)n_qtiles * BH;
   if (tiles > 0x7fffffffLL / 8) return DIT_ATTN_EINVAL;
@@ -159,12 +189,12 @@ int launch_pipe(const void* q, const void* k, const void* v, void* o, float* lse
   hipLaunchKernelGGL(attn_fwd_bf16_pipe_kernel<C>, dim3((unsigned)grid), dim3(C::kThreads), C::kLdsBytes, st,
                      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                      static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), lse, N, n_qtiles,
-                     scale_log2, scale, sp);
+                     scale_log2, scale, sp, L);
   hipError_t err = hipGetLastError();
   if (ws != nullptr) {
     if (err == hipSuccess) {
       hipLaunchKernelGGL(attn_split_combine_kernel, dim3((unsigned)(sp.n_split * (C::kBR / 8))), dim3(256), 0, st,
-                         sp.ws_o, sp.ws_lse, static_cast<uint16_t*>(o), lse, N, n_qtiles, sp);
+                         sp.ws_o, sp.ws_lse, static_cast<uint16_t*>(o), lse, N, n_qtiles, sp, L);
       err = hipGetLastError();
     }
     (void)hipFreeAsync(ws, st);
@@ -174,7 +204,7 @@ int launch_pipe(const void* q, const void* k, const void* v, void* o, float* lse
 
 template <class C>
 int launch_fp8(const void* q, const void* k, const void* v, void* o, float* lse, const float* descale,
-               int BH, int N, float scale, hipStream_t st, int n_cu) {
+               int BH, int N, float scale, hipStream_t st, int n_cu, const Layout& L) {
   const int n_qtiles = (N + C::kBR - 1) / C::kBR;
   const long long tiles = (long long)n_qtiles * BH;
   if (tiles > 0x7fffffffLL / 8) return DIT_ATTN_EINVAL;
@@ -201,12 +231,12 @@ int launch_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
   hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(C::kThreads), C::kLdsBytes, st,
                      static_cast<const uint8_t*>(q), static_cast<const uint8_t*>(k),
                      static_cast<const uint8_t*>(v), static_cast<uint16_t*>(o), lse, descale, N, n_qtiles,
-                     scale_log2, scale, sp);
+                     scale_log2, scale, sp, L);
   hipError_t err = hipGetLastError();
   if (ws != nullptr) {
     if (err == hipSuccess) {
       hipLaunchKernelGGL(attn_split_combine_kernel, dim3((unsigned)(sp.n_split * (C::kBR / 8))), dim3(256), 0, st,
-                         sp.ws_o, sp.ws_lse, static_cast<uint16_t*>(o), lse, N, n_qtiles, sp);
+                         sp.ws_o, sp.ws_lse, static_cast<uint16_t*>(o), lse, N, n_qtiles, sp, L);
       err = hipGetLastError();
     }
     (void)hipFreeAsync(ws, st);
@@ -218,7 +248,7 @@ int launch_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
 
 extern "C" {
 
-int dit_attn_version(void) { return (1 << 16) | 0; }
+int dit_attn_version(void) { return (1 << 16) | 1; }
 
 const char* dit_attn_strerror(int status) {
   switch (status) {
@@ -231,8 +261,9 @@ const char* dit_attn_strerror(int status) {
   }
 }
 
-int dit_attn_fwd_ex(const void* q, const void* k, const void* v, void* o, int B, int H, int N, int d,
-                    float scale, int dtype, const float* descale_qkv, float* lse, void* stream) {
+int dit_attn_fwd_strided(const void* q, const void* k, const void* v, void* o, int B, int H, int N, int d,
+                         float scale, int dtype, const int64_t* qkv_strides, const int64_t* o_strides,
+                         const float* descale_qkv, float* lse, void* stream) {
   if (!q || !k || !v || !o) return DIT_ATTN_EINVAL;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16)) return DIT_ATTN_EINVAL;
   if (lse && !aligned(lse, 4)) return DIT_ATTN_EINVAL;
@@ -242,13 +273,21 @@ int dit_attn_fwd_ex(const void* q, const void* k, const void* v, void* o, int B,
   if (dtype != DIT_ATTN_BF16 && dtype != DIT_ATTN_FP8_E4M3) return DIT_ATTN_EUNSUPPORTED;
   if (dtype == DIT_ATTN_BF16 && d != 64 && d != 128) return DIT_ATTN_EUNSUPPORTED;
   if (dtype == DIT_ATTN_FP8_E4M3 && d != 128) return DIT_ATTN_EUNSUPPORTED;
-  // element count B*H*N*d < 2^62 without overflow (each factor < 2^31)
-  const unsigned __int128 elems = (unsigned __int128)B * (unsigned)H * (unsigned)N * (unsigned)d;
-  if (elems >= ((unsigned __int128)1 << 62)) return DIT_ATTN_EINVAL;
   const long long bh = (long long)B * H;
   if (bh > 0x7fffffffLL) return DIT_ATTN_EINVAL;
-  const uint64_t in_bytes = (uint64_t)elems * (dtype == DIT_ATTN_BF16 ? 2u : 1u);
-  const uint64_t out_bytes = (uint64_t)elems * 2u;
+  // contiguous [B][H][N][d] unless strides are given (larger than any valid
+  // stride when H N d does not fit, which check_strides then rejects)
+  const unsigned __int128 hnd = (unsigned __int128)(unsigned)H * (unsigned)N * (unsigned)d;
+  const int64_t big = (int64_t)1 << 41;
+  const int64_t contig[3] = {hnd < (unsigned __int128)big ? (int64_t)hnd : big, (int64_t)N * d, d};
+  const int64_t* si = qkv_strides ? qkv_strides : contig;
+  const int64_t* so = o_strides ? o_strides : contig;
+  const unsigned in_size = dtype == DIT_ATTN_BF16 ? 2u : 1u;
+  uint64_t in_bytes = 0, out_bytes = 0;
+  if (!check_strides(si, B, H, N, d, in_size, false, &in_bytes)) return DIT_ATTN_EINVAL;
+  if (!check_strides(so, B, H, N, d, 2u, true, &out_bytes)) return DIT_ATTN_EINVAL;
+  // a 128-key tile of q, k or v must span < 2^31 bytes (32-bit DMA offsets)
+  if (si[2] * (int64_t)in_size * 128 >= ((int64_t)1 << 31)) return DIT_ATTN_EINVAL;
   if (overlap(o, out_bytes, q, in_bytes) || overlap(o, out_bytes, k, in_bytes) ||
       overlap(o, out_bytes, v, in_bytes))
     return DIT_ATTN_EINVAL;
@@ -260,12 +299,18 @@ int dit_attn_fwd_ex(const void* q, const void* k, const void* v, void* o, int B,
   }
   const int dev_status = check_device();
   if (dev_status != DIT_ATTN_OK) return dev_status;
+  const Layout L{si[0], si[1], si[2], so[0], so[1], so[2], H};
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (dtype == DIT_ATTN_BF16) {
-    if (d == 128) return launch_pipe<CfgBf16D128>(q, k, v, o, lse, (int)bh, N, scale, st, cu_count());
-    return launch_bf16<CfgBf16D64>(q, k, v, o, lse, (int)bh, N, scale, st);
+    if (d == 128) return launch_pipe<CfgBf16D128>(q, k, v, o, lse, (int)bh, N, scale, st, cu_count(), L);
+    return launch_bf16<CfgBf16D64>(q, k, v, o, lse, (int)bh, N, scale, st, L);
   }
-  return launch_fp8<CfgFp8D128>(q, k, v, o, lse, descale_qkv, (int)bh, N, scale, st, cu_count());
+  return launch_fp8<CfgFp8D128>(q, k, v, o, lse, descale_qkv, (int)bh, N, scale, st, cu_count(), L);
+}
+
+int dit_attn_fwd_ex(const void* q, const void* k, const void* v, void* o, int B, int H, int N, int d,
+                    float scale, int dtype, const float* descale_qkv, float* lse, void* stream) {
+  return dit_attn_fwd_strided(q, k, v, o, B, H, N, d, scale, dtype, nullptr, nullptr, descale_qkv, lse, stream);
 }
 
 int dit_attn_fwd(const void* q, const void* k, const void* v, void* o, int B, int H, int N, int d, float scale,

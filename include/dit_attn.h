@@ -106,6 +106,29 @@ DIT_ATTN_API int dit_attn_fwd_ex(const void* q, const void* k, const void* v, vo
                     const float* descale_qkv, float* lse, void* stream);
 
 /*
+ * dit_attn_fwd_strided - dit_attn_fwd_ex for rows that are not packed as
+ * [B][H][N][d]: the layout a fused QKV projection or a sequence-to-head
+ * all-to-all emits, e.g. [B][N][H][d] or [B][N][3][H][d].
+ *
+ * qkv_strides : host int64[3] {batch, head, token}: element strides shared by
+ *               q, k and v (the d values of a row are contiguous). NULL means
+ *               contiguous [B][H][N][d]: {H*N*d, N*d, d}. token >= d; batch and
+ *               head may be 0 (rows shared across heads or batch entries).
+ * o_strides   : host int64[3], the same for o; NULL means contiguous. The map
+ *               (b, h, n) -> row must be one to one (checked).
+ * Every stride times the element size (2 bytes bf16, 1 byte e4m3 for q, k, v;
+ * 2 bytes for o) must be a multiple of 16 bytes, each stride at most 2^40, and
+ * the token stride of q, k, v below 2^31 / (128 * element size). The
+ * aliasing checks of dit_attn_fwd use the byte spans the strides cover. lse
+ * stays packed as [B][H][N]. Other arguments and statuses as for
+ * dit_attn_fwd_ex (DIT_ATTN_EINVAL for a stride that breaks these rules).
+ */
+DIT_ATTN_API int dit_attn_fwd_strided(const void* q, const void* k, const void* v, void* o,
+                         int B, int H, int N, int d, float scale, int dtype,
+                         const int64_t* qkv_strides, const int64_t* o_strides,
+                         const float* descale_qkv, float* lse, void* stream);
+
+/*
  * dit_attn_quantize_e4m3 - per-tensor absmax quantisation of a bf16 tensor.
  *
  * Produces the fp8 inputs of the DIT_ATTN_FP8_E4M3 path on the device:
@@ -128,7 +151,7 @@ DIT_ATTN_API int dit_attn_quantize_e4m3(const void* x, int64_t n, void* x8, floa
 /* Human-readable name of a status code (static string, never NULL). */
 DIT_ATTN_API const char* dit_attn_strerror(int status);
 
-/* Library ABI version: (major << 16) | minor. */
+/* Library ABI version: (major << 16) | minor (1.1 adds dit_attn_fwd_strided). */
 DIT_ATTN_API int dit_attn_version(void);
 
 #ifdef __cplusplus

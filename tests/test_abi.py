@@ -23,8 +23,8 @@ def lib():
 
 
 def test_header_declares_the_entry_points():
-    assert _declared() == sorted(["dit_attn_fwd", "dit_attn_fwd_ex", "dit_attn_quantize_e4m3",
-                                  "dit_attn_strerror", "dit_attn_version"])
+    assert _declared() == sorted(["dit_attn_fwd", "dit_attn_fwd_ex", "dit_attn_fwd_strided",
+                                  "dit_attn_quantize_e4m3", "dit_attn_strerror", "dit_attn_version"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -69,6 +69,47 @@ A, B_, C, O = 0x10000, 0x20000, 0x30000, 0x40000   # fake, aligned, disjoint add
 def test_fwd_rejects_bad_arguments_before_launch(lib, args, expect):
     assert lib.dit_attn_fwd(*args, None) == expect
     assert lib.dit_attn_fwd_ex(*args, None, None, None) == expect
+
+
+def test_fwd_rejects_bad_arguments_strided_too(lib):
+    for args, expect in [((0, B_, C, O, 1, 1, 8, 64, 0.125, 0), -1), ((A, B_, C, O, 1, 1, 8, 96, 0.125, 0), -2)]:
+        assert lib.dit_attn_fwd_strided(*args, None, None, None, None, None) == expect
+
+
+# (B, H, N, d) = (2, 3, 8, 64) bf16 at disjoint fake addresses 16 MiB apart
+SA, SB, SC, SO = 0x1000000, 0x2000000, 0x3000000, 0x4000000
+BNHD = (8 * 3 * 64, 64, 3 * 64)              # [B][N][H][d]
+
+
+@pytest.mark.parametrize("qkv,o,expect,why", [
+    (BNHD, None, -3, "[B][N][H][d] inputs are valid (no GPU here: device error)"),
+    (BNHD, BNHD, -3, "[B][N][H][d] output too"),
+    ((8 * 9 * 64, 64, 9 * 64), None, -3, "token stride past H d (fused QKV buffer)"),
+    ((0, 0, 64), None, -3, "inputs may share rows across batch and heads"),
+    ((8 * 3 * 64, 64, 32), None, -1, "token stride below d"),
+    ((8 * 3 * 64, 64, 3 * 64 + 4), None, -1, "row start not 16-byte aligned (bf16: stride % 8)"),
+    ((-64, 64, 3 * 64), None, -1, "negative stride"),
+    (None, (0, 64, 3 * 64), -1, "output rows repeat across the batch"),
+    (None, (8 * 3 * 64, 64, 64), -1, "output heads overlap tokens"),
+    (None, (8 * 64, 2 * 8 * 64, 64), -3, "output: any one-to-one order of the dimensions ([H][B][N][d])"),
+    (None, (3 * 64, 8 * 3 * 64 * 2, 64), -1, "output batch stride inside the token range"),
+    ((2 ** 41, 64, 192), None, -1, "stride above 2^40"),
+    ((8 * 3 * 2 ** 24, 2 ** 24, 2 ** 24), None, -1, "a 128-token tile would pass 2^31 bytes"),
+])
+def test_strided_layout_checks(lib, qkv, o, expect, why):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present; layouts are run by the GPU tests")
+    st = lib.dit_attn_fwd_strided(SA, SB, SC, SO, 2, 3, 8, 64, 0.125, 0, qkv, o, None, None, None)
+    assert st == expect, why
+
+
+def test_strided_output_overlap_uses_the_span(lib):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    # o starts inside the span of a [B][N][H][d] v (v covers 2*8*3*64*2 bytes)
+    assert lib.dit_attn_fwd_strided(SA, SB, SC, SC + 4096, 2, 3, 8, 64, 0.125, 0, BNHD, None, None, None, None) == -1
 
 
 def test_fwd_ex_rejects_bad_lse(lib):
