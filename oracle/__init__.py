@@ -20,14 +20,20 @@ Pins (what each function is checked against, in tests/test_oracle*.py):
   dequantised inputs; the P rounding error obeys the e4m3 bound; closed forms
   with identical keys and N = 1; with the rounded denominator a constant V is
   returned exactly and rows differ from the default by one bounded factor.
+* ``attention_blocksparse``: torch's float64 CPU scaled-dot-product attention
+  with the boolean key mask (a library routine); full lists give
+  ``attention``; one listed block of one valid key gives that key's V row
+  and logit; the merge identity over two disjoint lists; permuted and
+  repeated list entries change nothing; empty lists give 0 / -inf.
 """
 from .attention import attention, attention_bruteforce, softmax_probabilities
 from .formats import (E4M3_MAX, bf16_round, e4m3_decode, e4m3_encode,
                       quantize_per_tensor)
+from .blocksparse import attention_blocksparse, key_set
 from .fp8_attention import P_SCALE, attention_fp8_pipeline
 
 __all__ = [
     "attention", "attention_bruteforce", "softmax_probabilities",
     "E4M3_MAX", "bf16_round", "e4m3_decode", "e4m3_encode", "quantize_per_tensor",
-    "P_SCALE", "attention_fp8_pipeline",
+    "P_SCALE", "attention_fp8_pipeline", "attention_blocksparse", "key_set",
 ]

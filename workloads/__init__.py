@@ -163,3 +163,41 @@ def dominating_key(B, H, N, d, j_star, seed=0, a=4.0, b=4.0):
     k[:, :, j_star, :] = (b * u).to(torch.bfloat16)
     v = torch.randn((B, H, N, d), generator=g).to(torch.bfloat16).contiguous()
     return q, k.contiguous(), v
+
+
+# ---------------------------------------------------------------- block lists
+def random_kv_blocks(B, H, N, density, seed=0, *, q_block=256, kv_block=64, n_text=512, max_blocks=None,
+                     empty_every=0):
+    """Seeded key-block lists for block-sparse attention.
+
+    For each (b, h, query block) the list holds every block of the first
+    ``n_text`` tokens (the text prompt, which each image token attends to)
+    and each remaining key block with probability ``density``, ascending.
+    The pages report a sparse attention mode without its selection rule, so
+    this pattern is only a stand-in with a plausible structure. With
+    ``empty_every`` = m > 0 every m-th query block (flat index) gets an empty
+    list. Returns (blocks int32 (B, H, nq, max_blocks) padded with -1,
+    counts int32 (B, H, nq)); max_blocks defaults to the longest list (>= 1).
+    """
+    nq = -(-N // q_block)
+    nk = -(-N // kv_block)
+    n_text_blocks = min(nk, -(-n_text // kv_block)) if n_text > 0 else 0
+    rng = np.random.default_rng(seed)
+    lists = []
+    for t in range(B * H * nq):
+        keep = np.zeros(nk, dtype=bool)
+        keep[:n_text_blocks] = True
+        keep[n_text_blocks:] = rng.random(nk - n_text_blocks) < density
+        if empty_every and t % empty_every == empty_every - 1:
+            keep[:] = False
+        lists.append(np.nonzero(keep)[0].astype(np.int32))
+    longest = max([1] + [x.size for x in lists])
+    mb = longest if max_blocks is None else max_blocks
+    assert mb >= longest
+    blocks = np.full((B * H * nq, mb), -1, dtype=np.int32)
+    counts = np.zeros(B * H * nq, dtype=np.int32)
+    for t, x in enumerate(lists):
+        blocks[t, :x.size] = x
+        counts[t] = x.size
+    return (torch.from_numpy(blocks.reshape(B, H, nq, mb)).contiguous(),
+            torch.from_numpy(counts.reshape(B, H, nq)).contiguous())
