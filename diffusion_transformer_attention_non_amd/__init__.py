@@ -12,12 +12,14 @@ import math
 
 from . import _lib
 from ._lib import (DIT_ATTN_BF16, DIT_ATTN_EDEVICE, DIT_ATTN_EINVAL, DIT_ATTN_ELAUNCH, DIT_ATTN_FP8_E4M3,
-                   DIT_ATTN_OK, DIT_ATTN_EUNSUPPORTED, dit_attn_fwd, dit_attn_fwd_ex, dit_attn_fwd_strided,
+                   DIT_ATTN_OK, DIT_ATTN_SPARSE_KV_BLOCK, DIT_ATTN_SPARSE_Q_BLOCK, DIT_ATTN_EUNSUPPORTED,
+                   dit_attn_fwd, dit_attn_fwd_blocksparse, dit_attn_fwd_ex, dit_attn_fwd_strided,
                    dit_attn_quantize_e4m3, dit_attn_strerror, dit_attn_version)
 
 __all__ = [
-    "DitAttnError", "attention", "quantize_e4m3", "dit_attn_fwd", "dit_attn_fwd_ex", "dit_attn_fwd_strided",
-    "dit_attn_quantize_e4m3",
+    "DitAttnError", "attention", "attention_blocksparse", "quantize_e4m3", "dit_attn_fwd", "dit_attn_fwd_ex",
+    "dit_attn_fwd_strided", "dit_attn_fwd_blocksparse", "dit_attn_quantize_e4m3", "DIT_ATTN_SPARSE_Q_BLOCK",
+    "DIT_ATTN_SPARSE_KV_BLOCK",
     "dit_attn_strerror", "dit_attn_version", "DIT_ATTN_BF16", "DIT_ATTN_FP8_E4M3", "DIT_ATTN_OK",
     "DIT_ATTN_EINVAL", "DIT_ATTN_EUNSUPPORTED", "DIT_ATTN_EDEVICE", "DIT_ATTN_ELAUNCH",
 ]
@@ -77,6 +79,50 @@ def attention(q, k, v, scale: float | None = None, *, out=None, lse=None, descal
                               descale, lse, _stream_handle(stream))
     if st != DIT_ATTN_OK:
         raise DitAttnError(st, "dit_attn_fwd_strided")
+    return out
+
+
+def attention_blocksparse(q, k, v, kv_blocks, kv_counts, scale: float | None = None, *, out=None, lse=None,
+                          stream=None):
+    """Attention in which each block of 256 queries visits only listed blocks of 64 keys.
+
+    q, k, v: bf16 (B, H, N, 128) device tensors, strided as for ``attention``.
+    kv_counts: int32 device tensor (B, H, ceil(N / 256)), the number of key
+    blocks listed for each query block; kv_blocks: int32 device tensor
+    (B, H, ceil(N / 256), max_blocks) whose first count entries per row are
+    strictly increasing key-block indices in [0, ceil(N / 64)). An empty list
+    gives zero output rows (and -inf in ``lse``)."""
+    import torch
+    if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v must share one (B, H, N, d) shape")
+    if q.dtype != torch.bfloat16 or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("block-sparse attention takes bf16 q, k, v")
+    for t in (q, k, v):
+        if not t.is_cuda or t.stride(3) != 1:
+            raise ValueError("q, k, v must be device tensors with a contiguous last dimension")
+    if k.stride() != q.stride() or v.stride() != q.stride():
+        raise ValueError("q, k, v must share strides")
+    B, H, N, d = q.shape
+    nq = -(-N // DIT_ATTN_SPARSE_Q_BLOCK)
+    if (kv_counts.shape != (B, H, nq) or kv_counts.dtype != torch.int32 or not kv_counts.is_contiguous()
+            or not kv_counts.is_cuda):
+        raise ValueError(f"kv_counts must be a contiguous int32 device tensor of shape {(B, H, nq)}")
+    if (kv_blocks.dim() != 4 or kv_blocks.shape[:3] != (B, H, nq) or kv_blocks.dtype != torch.int32
+            or not kv_blocks.is_contiguous() or not kv_blocks.is_cuda):
+        raise ValueError(f"kv_blocks must be a contiguous int32 device tensor of shape {(B, H, nq)} + (max_blocks,)")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=q.device)
+    elif out.shape != q.shape or out.dtype != torch.bfloat16 or not out.is_cuda or out.stride(3) != 1:
+        raise ValueError("out must be a bf16 device tensor of q's shape with a contiguous last dimension")
+    if lse is not None and (lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous()):
+        raise ValueError("lse must be a contiguous float32 (B, H, N) tensor")
+    st = dit_attn_fwd_blocksparse(q, k, v, out, B, H, N, d, float(scale), DIT_ATTN_BF16, kv_blocks, kv_counts,
+                                  kv_blocks.shape[3], q.stride()[:3], out.stride()[:3], lse,
+                                  _stream_handle(stream))
+    if st != DIT_ATTN_OK:
+        raise DitAttnError(st, "dit_attn_fwd_blocksparse")
     return out
 
 

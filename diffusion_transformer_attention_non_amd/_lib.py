@@ -19,8 +19,11 @@ DIT_ATTN_EUNSUPPORTED = -2
 DIT_ATTN_EDEVICE = -3
 DIT_ATTN_ELAUNCH = -4
 
-EXPORTED = ("dit_attn_fwd", "dit_attn_fwd_ex", "dit_attn_fwd_strided", "dit_attn_quantize_e4m3",
-            "dit_attn_strerror", "dit_attn_version")
+DIT_ATTN_SPARSE_Q_BLOCK = 256
+DIT_ATTN_SPARSE_KV_BLOCK = 64
+
+EXPORTED = ("dit_attn_fwd", "dit_attn_fwd_blocksparse", "dit_attn_fwd_ex", "dit_attn_fwd_strided",
+            "dit_attn_quantize_e4m3", "dit_attn_strerror", "dit_attn_version")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is not built; run `python -m diffusion_transformer_attention_non_amd.build` "
@@ -34,6 +37,9 @@ _lib.dit_attn_fwd_ex.argtypes = [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _vp
 _lib.dit_attn_fwd_ex.restype = _i
 _lib.dit_attn_fwd_strided.argtypes = [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _vp, _vp, _vp, _vp, _vp]
 _lib.dit_attn_fwd_strided.restype = _i
+_lib.dit_attn_fwd_blocksparse.argtypes = [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _vp, _vp, _i,
+                                          _vp, _vp, _vp, _vp]
+_lib.dit_attn_fwd_blocksparse.restype = _i
 _lib.dit_attn_quantize_e4m3.argtypes = [_vp, _i64, _vp, _vp, _vp, _vp]
 _lib.dit_attn_quantize_e4m3.restype = _i
 _lib.dit_attn_strerror.argtypes = [_i]
@@ -60,18 +66,29 @@ def dit_attn_fwd_ex(q, k, v, o, B, H, N, d, scale, dtype, descale_qkv=None, lse=
                                 _ptr(descale_qkv), _ptr(lse), _ptr(stream))
 
 
+def _strides3(s):
+    """(ctypes array that must outlive the call, its address) or (None, None)."""
+    if s is None:
+        return None, None
+    arr = (ctypes.c_int64 * 3)(*[int(x) for x in s])
+    return arr, ctypes.cast(arr, ctypes.c_void_p)
+
+
 def dit_attn_fwd_strided(q, k, v, o, B, H, N, d, scale, dtype, qkv_strides=None, o_strides=None,
                          descale_qkv=None, lse=None, stream=None) -> int:
-    qs, os_ = (ctypes.c_int64 * 3)(), (ctypes.c_int64 * 3)()
-    qp = op = None
-    if qkv_strides is not None:
-        qs[:] = [int(x) for x in qkv_strides]
-        qp = ctypes.cast(qs, ctypes.c_void_p)
-    if o_strides is not None:
-        os_[:] = [int(x) for x in o_strides]
-        op = ctypes.cast(os_, ctypes.c_void_p)
+    qs, qp = _strides3(qkv_strides)
+    os_, op = _strides3(o_strides)
     return _lib.dit_attn_fwd_strided(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, H, N, d, scale, dtype, qp, op,
                                      _ptr(descale_qkv), _ptr(lse), _ptr(stream))
+
+
+def dit_attn_fwd_blocksparse(q, k, v, o, B, H, N, d, scale, dtype, kv_blocks, kv_counts, max_blocks,
+                             qkv_strides=None, o_strides=None, lse=None, stream=None) -> int:
+    qs, qp = _strides3(qkv_strides)
+    os_, op = _strides3(o_strides)
+    return _lib.dit_attn_fwd_blocksparse(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, H, N, d, scale, dtype,
+                                         _ptr(kv_blocks), _ptr(kv_counts), max_blocks, qp, op, _ptr(lse),
+                                         _ptr(stream))
 
 
 def dit_attn_quantize_e4m3(x, n, x8, descale, amax_ws, stream=None) -> int:

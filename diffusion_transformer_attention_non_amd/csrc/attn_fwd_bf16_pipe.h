@@ -83,6 +83,16 @@ struct PipeSplit {
 template <bool B>
 using flag_t = std::integral_constant<bool, B>;
 
+// Block-sparse visiting: for query tile t of head bh (t over 256-row tiles),
+// the 64-key tiles list[(bh * n_qtiles + t) * max_blocks + i], i < count, in
+// ascending order, with count = counts[bh * n_qtiles + t] (at most
+// max_blocks). Unused by the dense form.
+struct KvBlocks {
+  const int* list;
+  const int* counts;
+  int max_blocks;
+};
+
 // 16 bytes per lane from a buffer into LDS at M0 + 16 * lane. Written as asm
 // so that the compiler does not order every later LDS read behind it (it
 // would wait for all loads in flight); completion is awaited explicitly with
@@ -93,12 +103,14 @@ __device__ __forceinline__ void dma_b128(i32x4_t rsrc, int voffset, unsigned lds
 
 #define DIT_FENCE() __builtin_amdgcn_sched_barrier(0)
 
-template <class C>
+// SPARSE: the key tiles come from a KvBlocks list instead of 0 .. n_t - 1
+// (no key-range split; every workgroup takes one query tile).
+template <class C, bool SPARSE = false>
 __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void attn_fwd_bf16_pipe_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
                                const uint16_t* __restrict__ Vg, uint16_t* __restrict__ Og,
                                float* __restrict__ LSEg, int N, int n_qtiles, float scale_log2, float scale,
-                               PipeSplit split, Layout L) {
+                               PipeSplit split, Layout L, KvBlocks kvb = KvBlocks{nullptr, nullptr, 0}) {
   constexpr int D = C::kD, KS = C::kKS, DB = C::kDB;
   constexpr int KROW = C::kKRow, VROW = C::kVRow;
   extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -120,6 +132,24 @@ void attn_fwd_bf16_pipe_kernel(const uint16_t* __restrict__ Qg, const uint16_t* 
   }
   const int bh = tile / n_qtiles;
   const int qt = tile - bh * n_qtiles;
+  // key tile at pipeline position p: p itself, or the p-th listed one. The
+  // pipeline looks up to three positions past the end; those clamp to the
+  // last entry (their data is never used).
+  // The list is read through the constant address space: scalar loads, which
+  // do not count against the vector-memory counter that orders the tile DMAs.
+  using cint = const __attribute__((address_space(4))) int;
+  cint* klist = nullptr;
+  if constexpr (SPARSE) {
+    const int cnt = *(cint*)(kvb.counts + tile);
+    u1 = cnt < 0 ? 0 : (cnt > kvb.max_blocks ? kvb.max_blocks : cnt);
+    klist = (cint*)(kvb.list + (size_t)tile * kvb.max_blocks);
+  }
+  auto ktile = [&](int p) __attribute__((always_inline)) {
+    if constexpr (SPARSE) return klist[p < u1 ? p : u1 - 1];
+    else return p;
+  };
+  // first key of sub-tile j (32 keys) of the pipeline
+  auto ksub = [&](int j) __attribute__((always_inline)) { return ktile(j >> 1) * 64 + (j & 1) * 32; };
   const long long ibase = L.in_off(bh), obase = L.out_off(bh);
   const int rowb = (int)(L.qn * 2);       // bytes between consecutive tokens of q, k, v
   const char* Kh = reinterpret_cast<const char*>(Kg + ibase);
@@ -130,6 +160,23 @@ void attn_fwd_bf16_pipe_kernel(const uint16_t* __restrict__ Qg, const uint16_t* 
   const int lane = tid & 63;
   const int l32 = lane & 31, hh = lane >> 5;
   const int q0 = qt * C::kBR + wave * 64;
+
+  if constexpr (SPARSE) {
+    if (u1 == 0) {
+      // no listed key: attention over the empty set gives O = 0, LSE = -inf
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        const int row = q0 + qb * 32 + l32;
+        if (row < N) {
+          uint16_t* orow = Og + obase + (long long)row * L.on + hh * (D / 2);
+#pragma unroll
+          for (int c = 0; c < D / 2; c += 8) *(i32x4_t*)(orow + c) = i32x4_t{0, 0, 0, 0};
+          if (LSEg != nullptr && hh == 0) LSEg[(size_t)bh * N + row] = -INFINITY;
+        }
+      }
+      return;
+    }
+  }
 
   bf16x8_t qf[2][KS];
 #pragma unroll
@@ -159,7 +206,13 @@ void attn_fwd_bf16_pipe_kernel(const uint16_t* __restrict__ Qg, const uint16_t* 
   }
   // buffer descriptor of one 64-key tile: the range check zero-fills rows past N
   auto tile_rsrc = [&](const char* head, int t) __attribute__((always_inline)) {
-    const int rows = min(64, N - t * 64);
+    int rows = min(64, N - t * 64);
+    if constexpr (SPARSE) {
+      // a listed index outside [0, n_t) (a malformed list) reads zeros
+      const bool inside = t >= 0 && t < n_t;
+      rows = inside ? rows : 0;
+      t = inside ? t : 0;
+    }
     const unsigned long long a = (unsigned long long)(head + (long long)t * 64 * rowb);
     i32x4_t rs;
     rs[0] = __builtin_amdgcn_readfirstlane((int)(unsigned)a);
@@ -216,7 +269,7 @@ void attn_fwd_bf16_pipe_kernel(const uint16_t* __restrict__ Qg, const uint16_t* 
   auto mask_keys = [&](int j, f32x16_t& s) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int key = j * 32 + (r >> 2) * 8 + hh * 4 + (r & 3);
+      const int key = ksub(j) + (r >> 2) * 8 + hh * 4 + (r & 3);
       s[r] = key < N ? s[r] : -INFINITY;
     }
   };
@@ -281,11 +334,11 @@ void attn_fwd_bf16_pipe_kernel(const uint16_t* __restrict__ Qg, const uint16_t* 
 
   // ---- prologue: K tiles u0..u0+2, V tiles u0, u0+1; the first sub-tile's
   // logits and their exact row maxima
-  dma_tile(Kh, u0, kslot(u0), kdo);
-  if (u0 + 1 < u1) dma_tile(Kh, u0 + 1, kslot(u0 + 1), kdo);
-  if (u0 + 2 < u1) dma_tile(Kh, u0 + 2, kslot(u0 + 2), kdo);
-  dma_tile(Vh, u0, vslot(u0), vdo);
-  if (u0 + 1 < u1) dma_tile(Vh, u0 + 1, vslot(u0 + 1), vdo);
+  dma_tile(Kh, ktile(u0), kslot(u0), kdo);
+  if (u0 + 1 < u1) dma_tile(Kh, ktile(u0 + 1), kslot(u0 + 1), kdo);
+  if (u0 + 2 < u1) dma_tile(Kh, ktile(u0 + 2), kslot(u0 + 2), kdo);
+  dma_tile(Vh, ktile(u0), vslot(u0), vdo);
+  if (u0 + 1 < u1) dma_tile(Vh, ktile(u0 + 1), vslot(u0 + 1), vdo);
   __builtin_amdgcn_s_waitcnt(0x0F70);      // vmcnt(0)
   __syncthreads();
   read_kfrags(2 * u0);
@@ -293,7 +346,7 @@ void attn_fwd_bf16_pipe_kernel(const uint16_t* __restrict__ Qg, const uint16_t* 
     f32x16_t s0;
     s_chain(0, s0);
     s_chain(1, s1);
-    if (32 * (2 * u0 + 1) > N) { mask_keys(2 * u0, s0); mask_keys(2 * u0, s1); }
+    if (ksub(2 * u0) + 32 > N) { mask_keys(2 * u0, s0); mask_keys(2 * u0, s1); }
     mc[0] = row_max(s0);
     mc[1] = row_max(s1);
 #pragma unroll
@@ -351,7 +404,7 @@ void attn_fwd_bf16_pipe_kernel(const uint16_t* __restrict__ Qg, const uint16_t* 
       }
     }
     if constexpr (MASK) {
-      if (32 * (j + 2) > N) mask_keys(j + 1, sa);
+      if (ksub(j + 1) + 32 > N) mask_keys(j + 1, sa);
     }
     // ================= phase Y: P_{j-1} V_{j-1} (keys 16-31), S_{j+1} block 1, P_j block 1
     {
@@ -376,7 +429,7 @@ void attn_fwd_bf16_pipe_kernel(const uint16_t* __restrict__ Qg, const uint16_t* 
       }
     }
     if constexpr (MASK) {
-      if (32 * (j + 2) > N) mask_keys(j + 1, sb);
+      if (ksub(j + 1) + 32 > N) mask_keys(j + 1, sb);
     }
     s1 = sb;
     // The packed P must exist here: without this the compiler sinks the bf16
@@ -391,7 +444,7 @@ void attn_fwd_bf16_pipe_kernel(const uint16_t* __restrict__ Qg, const uint16_t* 
         f32x16_t s;
         s_chain(qb, s);
         if constexpr (MASK) {
-          if (32 * (j + 1) > N) mask_keys(j, s);
+          if (ksub(j) + 32 > N) mask_keys(j, s);
         }
         const float m_new = fmaxf(mc[qb], row_max(s));
         const float alpha = fast_exp2(mc[qb] - m_new);
@@ -429,10 +482,12 @@ void attn_fwd_bf16_pipe_kernel(const uint16_t* __restrict__ Qg, const uint16_t* 
   // state (TAIL false) both DMAs exist and no key of tiles u, u+1 lies past N,
   // so the body has no branch but the rare path: a branch would let the
   // compiler sink the softmax work out of the MFMA phases.
-  auto iteration = [&](int u, auto tail_c) __attribute__((always_inline)) {
+  // tk, tv: the key tiles at positions u + 3 (K) and u + 2 (V); before_wait()
+  // runs after the compute, ahead of the wait for the tiles.
+  auto iteration = [&](int u, auto tail_c, int tk, int tv, auto&& before_wait) __attribute__((always_inline)) {
     constexpr bool TAIL = decltype(tail_c)::value;
     const bool k_next = !TAIL || u + 3 < u1, v_next = !TAIL || u + 2 < u1;
-    const i32x4_t rk = tile_rsrc(Kh, u + 3), rv = tile_rsrc(Vh, u + 2);
+    const i32x4_t rk = tile_rsrc(Kh, tk), rv = tile_rsrc(Vh, tv);
     const char* sk = kslot(u + 3);
     const char* sv = vslot(u + 2);
     DIT_FENCE();
@@ -451,6 +506,7 @@ void attn_fwd_bf16_pipe_kernel(const uint16_t* __restrict__ Qg, const uint16_t* 
       }
     });
     DIT_FENCE();
+    before_wait();
     if (TAIL)
       __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     else
@@ -461,8 +517,26 @@ void attn_fwd_bf16_pipe_kernel(const uint16_t* __restrict__ Qg, const uint16_t* 
   // Sub-tiles past u1 that the pipeline touches (S of sub-tile 2 u1) read a
   // slot that is stale or zero: their values are never used.
   int u = u0;
-  for (; u + 3 < u1; ++u) iteration(u, flag_t<false>{});
-  for (; u < u1; ++u) iteration(u, flag_t<true>{});
+  auto nothing = [] {};
+  if constexpr (SPARSE) {
+    // A steady-state iteration loads the next one's K tile index while it
+    // waits for its DMAs (a scalar load waited for at the top of the loop
+    // would stall every wave there).
+    int tk = ktile(u0 + 3), tv = ktile(u0 + 2);
+    for (; u + 3 < u1; ++u) {
+      int tk_next;
+      iteration(u, flag_t<false>{}, tk, tv, [&] {
+        tk_next = ktile(u + 4);
+        asm volatile("" : "+s"(tk_next));
+      });
+      tv = tk;
+      tk = tk_next;
+    }
+    for (; u < u1; ++u) iteration(u, flag_t<true>{}, ktile(u + 3), ktile(u + 2), nothing);
+  } else {
+    for (; u + 3 < u1; ++u) iteration(u, flag_t<false>{}, u + 3, u + 2, nothing);
+    for (; u < u1; ++u) iteration(u, flag_t<true>{}, u + 3, u + 2, nothing);
+  }
 
   // ---- P V of the last sub-tile (its V fragments were read in the last phase Y)
 #pragma unroll

@@ -38,7 +38,10 @@ hipError_t allow_lds_bf16() {
 }
 template <class C>
 hipError_t allow_lds_pipe() {
-  return hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_fwd_bf16_pipe_kernel<C>),
+  const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_fwd_bf16_pipe_kernel<C, false>),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, C::kLdsBytes);
+  if (e != hipSuccess) return e;
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_fwd_bf16_pipe_kernel<C, true>),
                              hipFuncAttributeMaxDynamicSharedMemorySize, C::kLdsBytes);
 }
 template <class C>
@@ -244,26 +247,17 @@ int launch_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
   return err == hipSuccess ? DIT_ATTN_OK : DIT_ATTN_ELAUNCH;
 }
 
-}  // namespace
+// What check_call derives from valid arguments.
+struct Checked {
+  Layout L;
+  int bh;
+  uint64_t in_bytes, out_bytes, lse_bytes;   // byte spans of q (k, v), o, lse
+};
 
-extern "C" {
-
-int dit_attn_version(void) { return (1 << 16) | 1; }
-
-const char* dit_attn_strerror(int status) {
-  switch (status) {
-    case DIT_ATTN_OK: return "ok";
-    case DIT_ATTN_EINVAL: return "invalid argument";
-    case DIT_ATTN_EUNSUPPORTED: return "unsupported head dimension or dtype";
-    case DIT_ATTN_EDEVICE: return "no gfx950 HIP device is current";
-    case DIT_ATTN_ELAUNCH: return "kernel launch failed";
-    default: return "unknown status";
-  }
-}
-
-int dit_attn_fwd_strided(const void* q, const void* k, const void* v, void* o, int B, int H, int N, int d,
-                         float scale, int dtype, const int64_t* qkv_strides, const int64_t* o_strides,
-                         const float* descale_qkv, float* lse, void* stream) {
+// Host checks shared by the attention entry points; no device call.
+int check_call(const void* q, const void* k, const void* v, void* o, int B, int H, int N, int d, float scale,
+               int dtype, const int64_t* qkv_strides, const int64_t* o_strides, const float* descale_qkv,
+               float* lse, Checked* c) {
   if (!q || !k || !v || !o) return DIT_ATTN_EINVAL;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16)) return DIT_ATTN_EINVAL;
   if (lse && !aligned(lse, 4)) return DIT_ATTN_EINVAL;
@@ -291,21 +285,80 @@ int dit_attn_fwd_strided(const void* q, const void* k, const void* v, void* o, i
   if (overlap(o, out_bytes, q, in_bytes) || overlap(o, out_bytes, k, in_bytes) ||
       overlap(o, out_bytes, v, in_bytes))
     return DIT_ATTN_EINVAL;
+  const uint64_t lse_bytes = (uint64_t)bh * (uint64_t)N * 4u;
   if (lse) {
-    const uint64_t lse_bytes = (uint64_t)bh * (uint64_t)N * 4u;
     if (overlap(lse, lse_bytes, q, in_bytes) || overlap(lse, lse_bytes, k, in_bytes) ||
         overlap(lse, lse_bytes, v, in_bytes) || overlap(lse, lse_bytes, o, out_bytes))
       return DIT_ATTN_EINVAL;
   }
+  *c = Checked{Layout{si[0], si[1], si[2], so[0], so[1], so[2], H}, (int)bh, in_bytes, out_bytes, lse_bytes};
+  return DIT_ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int dit_attn_version(void) { return (1 << 16) | 2; }
+
+const char* dit_attn_strerror(int status) {
+  switch (status) {
+    case DIT_ATTN_OK: return "ok";
+    case DIT_ATTN_EINVAL: return "invalid argument";
+    case DIT_ATTN_EUNSUPPORTED: return "unsupported head dimension or dtype";
+    case DIT_ATTN_EDEVICE: return "no gfx950 HIP device is current";
+    case DIT_ATTN_ELAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+int dit_attn_fwd_strided(const void* q, const void* k, const void* v, void* o, int B, int H, int N, int d,
+                         float scale, int dtype, const int64_t* qkv_strides, const int64_t* o_strides,
+                         const float* descale_qkv, float* lse, void* stream) {
+  Checked c;
+  const int status = check_call(q, k, v, o, B, H, N, d, scale, dtype, qkv_strides, o_strides, descale_qkv, lse, &c);
+  if (status != DIT_ATTN_OK) return status;
   const int dev_status = check_device();
   if (dev_status != DIT_ATTN_OK) return dev_status;
-  const Layout L{si[0], si[1], si[2], so[0], so[1], so[2], H};
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (dtype == DIT_ATTN_BF16) {
-    if (d == 128) return launch_pipe<CfgBf16D128>(q, k, v, o, lse, (int)bh, N, scale, st, cu_count(), L);
-    return launch_bf16<CfgBf16D64>(q, k, v, o, lse, (int)bh, N, scale, st, L);
+    if (d == 128) return launch_pipe<CfgBf16D128>(q, k, v, o, lse, c.bh, N, scale, st, cu_count(), c.L);
+    return launch_bf16<CfgBf16D64>(q, k, v, o, lse, c.bh, N, scale, st, c.L);
   }
-  return launch_fp8<CfgFp8D128>(q, k, v, o, lse, descale_qkv, (int)bh, N, scale, st, cu_count(), L);
+  return launch_fp8<CfgFp8D128>(q, k, v, o, lse, descale_qkv, c.bh, N, scale, st, cu_count(), c.L);
+}
+
+int dit_attn_fwd_blocksparse(const void* q, const void* k, const void* v, void* o, int B, int H, int N, int d,
+                             float scale, int dtype, const int32_t* kv_blocks, const int32_t* kv_counts,
+                             int max_blocks, const int64_t* qkv_strides, const int64_t* o_strides, float* lse,
+                             void* stream) {
+  Checked c;
+  const int status = check_call(q, k, v, o, B, H, N, d, scale, dtype, qkv_strides, o_strides, nullptr, lse, &c);
+  if (status != DIT_ATTN_OK) return status;
+  if (dtype != DIT_ATTN_BF16 || d != 128) return DIT_ATTN_EUNSUPPORTED;
+  if (!kv_blocks || !kv_counts || !aligned(kv_blocks, 4) || !aligned(kv_counts, 4)) return DIT_ATTN_EINVAL;
+  const int n_qtiles = (N + DIT_ATTN_SPARSE_Q_BLOCK - 1) / DIT_ATTN_SPARSE_Q_BLOCK;
+  const int n_t = (N + DIT_ATTN_SPARSE_KV_BLOCK - 1) / DIT_ATTN_SPARSE_KV_BLOCK;
+  if (max_blocks < 1 || max_blocks > n_t) return DIT_ATTN_EINVAL;
+  const long long tiles = (long long)c.bh * n_qtiles;
+  if (tiles > 0x7fffffffLL) return DIT_ATTN_EINVAL;
+  const uint64_t count_bytes = (uint64_t)tiles * 4u, list_bytes = count_bytes * (uint64_t)max_blocks;
+  // the lists are read-only inputs: they may share memory with q, k, v, not with what the call writes
+  if (overlap(o, c.out_bytes, kv_blocks, list_bytes) || overlap(o, c.out_bytes, kv_counts, count_bytes))
+    return DIT_ATTN_EINVAL;
+  if (lse && (overlap(lse, c.lse_bytes, kv_blocks, list_bytes) || overlap(lse, c.lse_bytes, kv_counts, count_bytes)))
+    return DIT_ATTN_EINVAL;
+  const int dev_status = check_device();
+  if (dev_status != DIT_ATTN_OK) return dev_status;
+  using C = CfgBf16D128;
+  static_assert(C::kBR == DIT_ATTN_SPARSE_Q_BLOCK, "query block = the kernel's query tile");
+  const PipeSplit sp{(int)tiles, 0, 1, nullptr, nullptr, nullptr};
+  const KvBlocks kvb{kv_blocks, kv_counts, max_blocks};
+  hipLaunchKernelGGL((attn_fwd_bf16_pipe_kernel<C, true>), dim3((unsigned)tiles), dim3(C::kThreads), C::kLdsBytes,
+                     static_cast<hipStream_t>(stream), static_cast<const uint16_t*>(q),
+                     static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o),
+                     lse, N, n_qtiles, scale * 1.4426950408889634f, scale, sp, c.L, kvb);
+  return hipGetLastError() == hipSuccess ? DIT_ATTN_OK : DIT_ATTN_ELAUNCH;
 }
 
 int dit_attn_fwd_ex(const void* q, const void* k, const void* v, void* o, int B, int H, int N, int d,

@@ -128,6 +128,49 @@ DIT_ATTN_API int dit_attn_fwd_strided(const void* q, const void* k, const void* 
                          const int64_t* qkv_strides, const int64_t* o_strides,
                          const float* descale_qkv, float* lse, void* stream);
 
+/* Tile sizes of dit_attn_fwd_blocksparse: query rows per list, keys per listed block. */
+#define DIT_ATTN_SPARSE_Q_BLOCK 256
+#define DIT_ATTN_SPARSE_KV_BLOCK 64
+
+/*
+ * dit_attn_fwd_blocksparse - attention in which each block of queries visits
+ * only a listed set of key/value blocks.
+ *
+ * The pages report a sparse attention mode for the DiT (Sol-Attention), run
+ * with the first 12 or 16 denoising steps dense, whose block-selection rule
+ * they do not give (Japanese summary, third paragraph). This call is the execution side only: the caller
+ * chooses the blocks; a dense step calls dit_attn_fwd instead. For query row
+ * i in query block t = i / 256 of head (b, h), with S the union of the listed
+ * key blocks (block u = keys 64u .. min(64u + 63, N - 1)):
+ *
+ *     O[b,h,i] = sum_{j in S} softmax_S(s_i)_j V[b,h,j],   s_ij = scale q_i . k_j
+ *
+ * and the LSE output is log(sum_{j in S} exp(s_ij)). An empty list gives
+ * O = 0 and LSE = -inf (attention over no keys).
+ *
+ * kv_counts  : device int32[B*H*ceil(N/256)]; entry (b*H + h)*ceil(N/256) + t
+ *              is the number of blocks listed for query block t of head (b, h).
+ *              Values above max_blocks are taken as max_blocks, negative ones
+ *              as 0. 4-byte aligned.
+ * kv_blocks  : device int32[B*H*ceil(N/256)][max_blocks]; the first count
+ *              entries of row (b*H + h)*ceil(N/256) + t are that list's key
+ *              block indices, strictly increasing, each in [0, ceil(N/64)).
+ *              Entries past the count are not read. 4-byte aligned.
+ * max_blocks : row length of kv_blocks, 1 <= max_blocks <= ceil(N/64).
+ * Neither list may overlap o or lse; they may share memory with q, k, v.
+ * Only dtype = DIT_ATTN_BF16 with d = 128 is implemented (else
+ * DIT_ATTN_EUNSUPPORTED). No key-range split: one workgroup per query block.
+ * Other arguments, layouts (qkv_strides, o_strides may be NULL) and statuses
+ * as for dit_attn_fwd_strided. A list that breaks the rules above cannot
+ * make the kernel access memory outside q, k, v, o, lse and the lists (a
+ * block index out of range reads zero rows), but its result is unspecified.
+ */
+DIT_ATTN_API int dit_attn_fwd_blocksparse(const void* q, const void* k, const void* v, void* o,
+                             int B, int H, int N, int d, float scale, int dtype,
+                             const int32_t* kv_blocks, const int32_t* kv_counts, int max_blocks,
+                             const int64_t* qkv_strides, const int64_t* o_strides,
+                             float* lse, void* stream);
+
 /*
  * dit_attn_quantize_e4m3 - per-tensor absmax quantisation of a bf16 tensor.
  *
@@ -151,7 +194,8 @@ DIT_ATTN_API int dit_attn_quantize_e4m3(const void* x, int64_t n, void* x8, floa
 /* Human-readable name of a status code (static string, never NULL). */
 DIT_ATTN_API const char* dit_attn_strerror(int status);
 
-/* Library ABI version: (major << 16) | minor (1.1 adds dit_attn_fwd_strided). */
+/* Library ABI version: (major << 16) | minor (1.1 adds dit_attn_fwd_strided,
+   1.2 dit_attn_fwd_blocksparse). */
 DIT_ATTN_API int dit_attn_version(void);
 
 #ifdef __cplusplus

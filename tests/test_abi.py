@@ -23,8 +23,9 @@ def lib():
 
 
 def test_header_declares_the_entry_points():
-    assert _declared() == sorted(["dit_attn_fwd", "dit_attn_fwd_ex", "dit_attn_fwd_strided",
-                                  "dit_attn_quantize_e4m3", "dit_attn_strerror", "dit_attn_version"])
+    assert _declared() == sorted(["dit_attn_fwd", "dit_attn_fwd_blocksparse", "dit_attn_fwd_ex",
+                                  "dit_attn_fwd_strided", "dit_attn_quantize_e4m3", "dit_attn_strerror",
+                                  "dit_attn_version"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -110,6 +111,45 @@ def test_strided_output_overlap_uses_the_span(lib):
         pytest.skip("a GPU is present")
     # o starts inside the span of a [B][N][H][d] v (v covers 2*8*3*64*2 bytes)
     assert lib.dit_attn_fwd_strided(SA, SB, SC, SC + 4096, 2, 3, 8, 64, 0.125, 0, BNHD, None, None, None, None) == -1
+
+
+# block-sparse: (B, H, N, d) = (1, 2, 1000, 128) bf16, 4 query blocks, 16 key blocks
+LB, LC = 0x5000000, 0x6000000
+
+
+@pytest.mark.parametrize("args,lists,expect,why", [
+    ((SA, SB, SC, SO, 1, 2, 1000, 128, 0.1, 0), (LB, LC, 16), -3, "valid (no GPU here: device error)"),
+    ((SA, SB, SC, SO, 1, 2, 1000, 128, 0.1, 0), (LB, LC, 1), -3, "max_blocks 1"),
+    ((SA, SB, SC, SO, 1, 2, 1000, 128, 0.1, 0), (0, LC, 16), -1, "NULL block list"),
+    ((SA, SB, SC, SO, 1, 2, 1000, 128, 0.1, 0), (LB, 0, 16), -1, "NULL counts"),
+    ((SA, SB, SC, SO, 1, 2, 1000, 128, 0.1, 0), (LB + 2, LC, 16), -1, "misaligned block list"),
+    ((SA, SB, SC, SO, 1, 2, 1000, 128, 0.1, 0), (LB, LC + 1, 16), -1, "misaligned counts"),
+    ((SA, SB, SC, SO, 1, 2, 1000, 128, 0.1, 0), (LB, LC, 0), -1, "max_blocks 0"),
+    ((SA, SB, SC, SO, 1, 2, 1000, 128, 0.1, 0), (LB, LC, 17), -1, "max_blocks above the key-block count"),
+    ((SA, SB, SC, SO, 1, 2, 1000, 128, 0.1, 0), (SO + 64, LC, 16), -1, "block list overlaps o"),
+    ((SA, SB, SC, SO, 1, 2, 1000, 128, 0.1, 0), (LB, SO, 16), -1, "counts alias o"),
+    ((SA, SB, SC, SO, 1, 2, 1000, 128, 0.1, 0), (SA, SB, 16), -3, "lists may share memory with inputs"),
+    ((SA, SB, SC, SO, 1, 2, 1000, 64, 0.1, 0), (LB, LC, 16), -2, "d = 64 not implemented"),
+    ((SA, SB, SC, SO, 1, 2, 1000, 128, 0.1, 1), (LB, LC, 16), -2, "fp8 not implemented"),
+    ((0, SB, SC, SO, 1, 2, 1000, 128, 0.1, 0), (LB, LC, 16), -1, "NULL q (shared checks)"),
+    ((SA, SB, SC, SO, 1, 2, 1000, 128, 0.0, 0), (LB, LC, 16), -1, "scale 0 (shared checks)"),
+])
+def test_blocksparse_checks(lib, args, lists, expect, why):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present; the block-sparse path is run by the GPU tests")
+    assert lib.dit_attn_fwd_blocksparse(*args, *lists, None, None, None, None) == expect, why
+
+
+def test_blocksparse_list_overlapping_lse(lib):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    lse = 0x7000000
+    args = (SA, SB, SC, SO, 1, 2, 1000, 128, 0.1, 0)
+    assert lib.dit_attn_fwd_blocksparse(*args, LB, LC, 16, None, None, lse, None) == -3
+    assert lib.dit_attn_fwd_blocksparse(*args, lse + 4000, LC, 16, None, None, lse, None) == -1
+    assert lib.dit_attn_fwd_blocksparse(*args, LB, lse + 8, 16, None, None, lse, None) == -1
 
 
 def test_fwd_ex_rejects_bad_lse(lib):
