@@ -117,13 +117,13 @@ void attn_fwd_bf16_pipe_kernel(const uint16_t* __restrict__ Qg, const uint16_t* 
 
   const int n_t = (N + 63) / 64;          // 64-key tiles
   // query tile and key-tile range [u0, u1) of this workgroup
-  int tile, u0 = 0, u1 = n_t, ws_index = -1;
+  int tile, u0 = 0, u1 = n_t, ws_index = -1, part = 0;
   if ((int)blockIdx.x < split.n_full) {
     tile = xcd_remap(blockIdx.x, split.n_full);
   } else {
     // neighbouring indices (one XCD) share a key range: K/V reuse in L2
     const int sidx = xcd_remap(blockIdx.x - split.n_full, gridDim.x - split.n_full);
-    const int part = sidx / split.n_split;
+    part = sidx / split.n_split;
     const int ti = sidx - part * split.n_split;
     tile = split.n_full + ti;
     u0 = part * n_t / split.parts;
@@ -140,8 +140,12 @@ void attn_fwd_bf16_pipe_kernel(const uint16_t* __restrict__ Qg, const uint16_t* 
   using cint = const __attribute__((address_space(4))) int;
   cint* klist = nullptr;
   if constexpr (SPARSE) {
+    // a split tile's parts take contiguous ranges of list positions
     const int cnt = *(cint*)(kvb.counts + tile);
-    u1 = cnt < 0 ? 0 : (cnt > kvb.max_blocks ? kvb.max_blocks : cnt);
+    const int c = cnt < 0 ? 0 : (cnt > kvb.max_blocks ? kvb.max_blocks : cnt);
+    const int parts = ws_index >= 0 ? split.parts : 1;   // an unsplit tile takes the whole list
+    u0 = part * c / parts;
+    u1 = (part + 1) * c / parts;
     klist = (cint*)(kvb.list + (size_t)tile * kvb.max_blocks);
   }
   auto ktile = [&](int p) __attribute__((always_inline)) {
@@ -162,12 +166,19 @@ void attn_fwd_bf16_pipe_kernel(const uint16_t* __restrict__ Qg, const uint16_t* 
   const int q0 = qt * C::kBR + wave * 64;
 
   if constexpr (SPARSE) {
-    if (u1 == 0) {
+    if (u1 <= u0) {
       // no listed key: attention over the empty set gives O = 0, LSE = -inf
+      // (for a part of a split tile: zero rows of weight 2^-inf)
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
         const int row = q0 + qb * 32 + l32;
-        if (row < N) {
+        if (ws_index >= 0) {
+          const int r = wave * 64 + qb * 32 + l32;
+          float* orow = split.ws_o + ((size_t)ws_index * C::kBR + r) * D + hh * (D / 2);
+#pragma unroll
+          for (int c = 0; c < D / 2; c += 4) *(f32x4_t*)(orow + c) = f32x4_t{0.f, 0.f, 0.f, 0.f};
+          if (hh == 0) split.ws_lse[(size_t)ws_index * C::kBR + r] = -INFINITY;
+        } else if (row < N) {
           uint16_t* orow = Og + obase + (long long)row * L.on + hh * (D / 2);
 #pragma unroll
           for (int c = 0; c < D / 2; c += 8) *(i32x4_t*)(orow + c) = i32x4_t{0, 0, 0, 0};
@@ -610,6 +621,12 @@ __global__ __launch_bounds__(256) void attn_split_combine_kernel(const float* __
   if (row >= N) return;
   float mx = -INFINITY;
   for (int p = 0; p < split.parts; ++p) mx = fmaxf(mx, ws_lse[(size_t)(p * split.n_split + ti) * BR + r]);
+  if (mx == -INFINITY) {
+    // every part empty (block-sparse lists only): attention over no key
+    *(uint2*)(Og + L.out_off(bh) + (long long)row * L.on + c) = uint2{0u, 0u};
+    if (LSEg != nullptr && c == 0) LSEg[(size_t)bh * N + row] = -INFINITY;
+    return;
+  }
   float wsum = 0.f;
   f32x4_t o = {0.f, 0.f, 0.f, 0.f};
   float lse_mx = mx, lse_sum = 0.f;    // the LSE output's own sums when ws_lse_out is given

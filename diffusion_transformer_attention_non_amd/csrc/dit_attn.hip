@@ -168,16 +168,19 @@ int plan_split(int BH, int n_qtiles, int N, int key_tile, int n_cu, PipeSplit* s
   return 1;
 }
 
-template <class C>
+// SPARSE: block lists in kvb; the split planner then takes max_blocks as
+// the key-tile count (the host never reads the lists).
+template <class C, bool SPARSE = false>
 int launch_pipe(const void* q, const void* k, const void* v, void* o, float* lse, int BH, int N,
-                float scale, hipStream_t st, int n_cu, const Layout& L) {
+                float scale, hipStream_t st, int n_cu, const Layout& L, const KvBlocks& kvb = KvBlocks{}) {
   const int n_qtiles = (N + C::kBR - 1) / C::kBR;
   const long long tiles = (long long)n_qtiles * BH;
   if (tiles > 0x7fffffffLL / 8) return DIT_ATTN_EINVAL;
   const float scale_log2 = scale * 1.4426950408889634f;
   PipeSplit sp;
   void* ws = nullptr;
-  if (plan_split(BH, n_qtiles, N, 64, n_cu, &sp)) {
+  const int keys_planned = SPARSE ? kvb.max_blocks * 64 : N;
+  if (plan_split(BH, n_qtiles, keys_planned, 64, n_cu, &sp)) {
     const size_t units = (size_t)sp.n_split * sp.parts * C::kBR;
     if (hipMallocAsync(&ws, units * (C::kD + 1) * sizeof(float), st) == hipSuccess && ws != nullptr) {
       sp.ws_o = static_cast<float*>(ws);
@@ -189,10 +192,11 @@ int launch_pipe(const void* q, const void* k, const void* v, void* o, float* lse
     }
   }
   const long long grid = (long long)sp.n_full + (long long)sp.n_split * sp.parts;
-  hipLaunchKernelGGL(attn_fwd_bf16_pipe_kernel<C>, dim3((unsigned)grid), dim3(C::kThreads), C::kLdsBytes, st,
+  auto* kernel = &attn_fwd_bf16_pipe_kernel<C, SPARSE>;
+  hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(C::kThreads), C::kLdsBytes, st,
                      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                      static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), lse, N, n_qtiles,
-                     scale_log2, scale, sp, L);
+                     scale_log2, scale, sp, L, kvb);
   hipError_t err = hipGetLastError();
   if (ws != nullptr) {
     if (err == hipSuccess) {
@@ -341,7 +345,7 @@ int dit_attn_fwd_blocksparse(const void* q, const void* k, const void* v, void* 
   const int n_t = (N + DIT_ATTN_SPARSE_KV_BLOCK - 1) / DIT_ATTN_SPARSE_KV_BLOCK;
   if (max_blocks < 1 || max_blocks > n_t) return DIT_ATTN_EINVAL;
   const long long tiles = (long long)c.bh * n_qtiles;
-  if (tiles > 0x7fffffffLL) return DIT_ATTN_EINVAL;
+  if (tiles > 0x7fffffffLL / 8) return DIT_ATTN_EINVAL;
   const uint64_t count_bytes = (uint64_t)tiles * 4u, list_bytes = count_bytes * (uint64_t)max_blocks;
   // the lists are read-only inputs: they may share memory with q, k, v, not with what the call writes
   if (overlap(o, c.out_bytes, kv_blocks, list_bytes) || overlap(o, c.out_bytes, kv_counts, count_bytes))
@@ -352,13 +356,9 @@ int dit_attn_fwd_blocksparse(const void* q, const void* k, const void* v, void* 
   if (dev_status != DIT_ATTN_OK) return dev_status;
   using C = CfgBf16D128;
   static_assert(C::kBR == DIT_ATTN_SPARSE_Q_BLOCK, "query block = the kernel's query tile");
-  const PipeSplit sp{(int)tiles, 0, 1, nullptr, nullptr, nullptr};
   const KvBlocks kvb{kv_blocks, kv_counts, max_blocks};
-  hipLaunchKernelGGL((attn_fwd_bf16_pipe_kernel<C, true>), dim3((unsigned)tiles), dim3(C::kThreads), C::kLdsBytes,
-                     static_cast<hipStream_t>(stream), static_cast<const uint16_t*>(q),
-                     static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o),
-                     lse, N, n_qtiles, scale * 1.4426950408889634f, scale, sp, c.L, kvb);
-  return hipGetLastError() == hipSuccess ? DIT_ATTN_OK : DIT_ATTN_ELAUNCH;
+  return launch_pipe<C, true>(q, k, v, o, lse, c.bh, N, scale, static_cast<hipStream_t>(stream), cu_count(), c.L,
+                              kvb);
 }
 
 int dit_attn_fwd_ex(const void* q, const void* k, const void* v, void* o, int B, int H, int N, int d,

@@ -159,7 +159,10 @@ DIT_ATTN_API int dit_attn_fwd_strided(const void* q, const void* k, const void* 
  * max_blocks : row length of kv_blocks, 1 <= max_blocks <= ceil(N/64).
  * Neither list may overlap o or lse; they may share memory with q, k, v.
  * Only dtype = DIT_ATTN_BF16 with d = 128 is implemented (else
- * DIT_ATTN_EUNSUPPORTED). No key-range split: one workgroup per query block.
+ * DIT_ATTN_EUNSUPPORTED). The last, partly filled round of workgroups is
+ * split as in dit_attn_fwd, over list positions instead of key tiles (the
+ * planner takes max_blocks as the list length, as the host never reads the
+ * lists), with the same stream-ordered scratch buffer.
  * Other arguments, layouts (qkv_strides, o_strides may be NULL) and statuses
  * as for dit_attn_fwd_strided. A list that breaks the rules above cannot
  * make the kernel access memory outside q, k, v, o, lse and the lists (a

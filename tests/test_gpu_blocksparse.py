@@ -137,6 +137,43 @@ def test_full_lists_equal_dense_bitwise(B, H, N):
     assert torch.equal(o, od) and torch.equal(l, ld)
 
 
+def test_full_lists_equal_dense_bitwise_with_split():
+    """B 2, H 24, N 4608: 864 query tiles, so the last round is split into key
+    ranges; with every block listed the sparse call splits the same way."""
+    B, H, N, d = 2, 24, 4608, 128
+    dit = _dit()
+    q, k, v = (t.to(DEV) for t in random_qkv(B, H, N, d, seed=335))
+    nq, nk = N // 256, N // 64
+    blocks = torch.arange(nk, dtype=torch.int32).expand(B, H, nq, nk).contiguous()
+    counts = torch.full((B, H, nq), nk, dtype=torch.int32)
+    say(f"[gpu] blocksparse full lists vs dense (split) B={B} H={H} N={N}")
+    o, l = _sparse(q, k, v, blocks, counts, 1 / math.sqrt(d))
+    ld = torch.empty_like(l)
+    od = dit.attention(q, k, v, 1 / math.sqrt(d), lse=ld)
+    torch.cuda.synchronize()
+    assert torch.equal(o, od) and torch.equal(l, ld)
+
+
+def test_blocksparse_split_parts_with_short_lists():
+    """H 3, N 4608: 54 query tiles, each split into key ranges (list
+    positions). Lists of 0 to 8 blocks against max_blocks 72 leave many parts
+    empty, and a tile with every part empty."""
+    B, H, N, d = 1, 3, 4608, 128
+    q, k, v = random_qkv(B, H, N, d, seed=350)
+    nq, nk = N // 256, N // 64
+    rng = np.random.default_rng(35)
+    blocks = np.full((B, H, nq, nk), -1, dtype=np.int32)
+    counts = np.zeros((B, H, nq), dtype=np.int32)
+    for h in range(H):
+        for t in range(nq):
+            c = int(rng.integers(0, 9))
+            blocks[0, h, t, :c] = np.sort(rng.choice(nk, c, replace=False))
+            counts[0, h, t] = c
+    counts[0, 0, 0] = 0
+    say(f"[gpu] blocksparse split parts, short lists H={H} N={N}")
+    _compare(q, k, v, torch.from_numpy(blocks), torch.from_numpy(counts), 1 / math.sqrt(d), "short lists")
+
+
 def test_blocksparse_bnhd_rows_and_lse_optional():
     B, H, N, d = 2, 3, 700, 128
     q, k, v = random_qkv(B, H, N, d, seed=340)
