@@ -10,6 +10,9 @@ uses the per-launch kernel time from events recorded on the stream the
 kernel runs on. ``cpu_baseline`` times the fp64 CPU oracle on a bounded
 sample of query rows of the same workload (each output row depends on one
 query row, so a row sample is the same computation, only fewer rows).
+``fp8`` and ``blocksparse`` are companion figures of the same workload: the
+e4m3 path, and block-sparse attention over the text key blocks plus a seeded
+fraction of the image key blocks (TFLOP/s over the keys actually visited).
 """
 from __future__ import annotations
 
@@ -111,6 +114,8 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="t2i_2048")
     ap.add_argument("--no-fp8", action="store_true", help="skip the fp8-e4m3 companion measurement")
+    ap.add_argument("--sparse-density", type=float, default=0.25,
+                    help="fraction of image key blocks in the block-sparse companion's lists (0 skips it)")
     ap.add_argument("--layout", choices=["bhnd", "bnhd"], default="bhnd",
                     help="rows of q, k, v and o packed as [B][H][N][d] (default) or taken from [B][N][H][d] "
                          "buffers through dit_attn_fwd_strided")
@@ -212,6 +217,38 @@ def main(argv=None):
                                     "peak": PEAK_TFLOPS["fp8"], "unit": "TFLOP/s",
                                     "frac": round(flops / (k8_mean * 1e-3) / 1e12 / PEAK_TFLOPS["fp8"], 4),
                                     "traffic": load_traffic("attn_fwd_fp8", w.name)}}
+
+    if args.sparse_density > 0 and args.layout == "bhnd" and d == 128:
+        from workloads import random_kv_blocks
+        blocks, counts = random_kv_blocks(B, H, N, args.sparse_density, seed=w.seed)
+        # keys each query row visits, summed over rows (the listed blocks' real sizes)
+        nq, mb = counts.shape[-1], blocks.shape[-1]
+        visited = 0
+        for bh in range(B * H):
+            for t in range(nq):
+                c = int(counts.view(-1, nq)[bh, t])
+                keys = sum(min(64, N - 64 * u) for u in blocks.view(-1, nq, mb)[bh, t, :c].tolist())
+                visited += min(256, N - 256 * t) * keys
+        blocks_d, counts_d = blocks.to(dev), counts.to(dev)
+
+        def step_sparse():
+            st = dit.dit_attn_fwd_blocksparse(qd, kd, vd, od, B, H, N, d, scale, dit.DIT_ATTN_BF16, blocks_d,
+                                              counts_d, mb, None, None, None, handle)
+            if st != 0:
+                raise dit.DitAttnError(st, "dit_attn_fwd_blocksparse")
+
+        walls, pers = time_launches(step_sparse, args.warmup, args.steps)
+        sflops = 4.0 * d * visited
+        ks_mean = statistics.fmean(pers)
+        line["blocksparse"] = {
+            "workload": f"{w.name}, text blocks + {args.sparse_density:.2f} of image key blocks per 256-query block",
+            "visited_fraction": round(visited / (B * H * N * N), 4),
+            "value": round(sflops / (walls / args.steps) / 1e12, 2), "unit": "TFLOP/s over visited keys",
+            "ms_per_step": round(walls / args.steps * 1e3, 4),
+            "speedup_vs_dense": round((wall / args.steps) / (walls / args.steps), 3),
+            "roofline": {"bound": "mfma", "achieved": round(sflops / (ks_mean * 1e-3) / 1e12, 2), "peak": peak,
+                         "unit": "TFLOP/s", "frac": round(sflops / (ks_mean * 1e-3) / 1e12 / peak, 4),
+                         "traffic": None}}
 
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(q, k, v, scale, args.cpu_budget)
