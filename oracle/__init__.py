@@ -25,15 +25,25 @@ Pins (what each function is checked against, in tests/test_oracle*.py):
   ``attention``; one listed block of one valid key gives that key's V row
   and logit; the merge identity over two disjoint lists; permuted and
   repeated list entries change nothing; empty lists give 0 / -inf.
+* ``mx_quantize``: torch's float8_e4m3fn cast of each value divided by its
+  block's power of two; the block maximum's code in the top binade; the
+  half-step error bound; power-of-two invariance; exact blocks; zero blocks;
+  the token-blocked scale layout on columns of known magnitude.
+* ``attention_mx_pipeline``: with P unrounded it equals ``attention`` on the
+  dequantised inputs; with every scale 2^0 it equals
+  ``attention_fp8_pipeline`` with unit descales; doubling every V scale
+  doubles O; moving 2^k from ``scale`` into every Q scale changes nothing.
 """
 from .attention import attention, attention_bruteforce, softmax_probabilities
 from .formats import (E4M3_MAX, bf16_round, e4m3_decode, e4m3_encode,
                       quantize_per_tensor)
 from .blocksparse import attention_blocksparse, key_set
 from .fp8_attention import P_SCALE, attention_fp8_pipeline
+from .mx import attention_mx_pipeline, mx_dequantize, mx_quantize, shared_exponent
 
 __all__ = [
     "attention", "attention_bruteforce", "softmax_probabilities",
     "E4M3_MAX", "bf16_round", "e4m3_decode", "e4m3_encode", "quantize_per_tensor",
     "P_SCALE", "attention_fp8_pipeline", "attention_blocksparse", "key_set",
+    "attention_mx_pipeline", "mx_dequantize", "mx_quantize", "shared_exponent",
 ]

@@ -34,6 +34,15 @@ def attention_fp8_pipeline(q8, k8, v8, dq, dk, dv, scale, rows=None, block=512,
     q = e4m3_decode(q8) * np.float64(dq)
     k = e4m3_decode(k8) * np.float64(dk)
     v = e4m3_decode(v8)
+    return pipeline_on_values(q, k, v, dv, scale, rows=rows, block=block, p_scale=p_scale, round_p=round_p,
+                              den_rounded=den_rounded)
+
+
+def pipeline_on_values(q, k, v, dv, scale, rows=None, block=512, p_scale=P_SCALE, round_p=True,
+                       den_rounded=False):
+    """The pipeline after the inputs are dequantised: q, k, v float64 (B, H, N, d)
+    values, dv the factor O carries. Shared by the per-tensor and the
+    block-scaled (MX) input formats."""
     B, H, N, d = q.shape
     idx = np.arange(N) if rows is None else np.asarray(rows, dtype=np.int64)
     R = idx.size
