@@ -31,7 +31,8 @@ sys.path.insert(0, ROOT)
 METRIC = "DiT attention fwd TFLOP/s at 16896-token shape; % of MI355X MFMA peak"
 PEAK_TFLOPS = {"bf16": 2516.6, "fp8": 5033.2}     # MI355X dense MFMA, 2.4 GHz
 HBM_PEAK_GBS = 8000.0
-KERNEL_SOURCES = ["attn_common.h", "attn_fwd_bf16.h", "attn_fwd_bf16_pipe.h", "attn_fwd_fp8_pipe.h", "dit_attn.hip"]
+KERNEL_SOURCES = ["attn_common.h", "attn_fwd_bf16.h", "attn_fwd_bf16_pipe.h", "attn_fwd_fp8_pipe.h", "quant_mx.h",
+                  "dit_attn.hip"]
 
 
 def kernel_source_hash() -> str:

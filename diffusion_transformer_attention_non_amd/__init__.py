@@ -12,14 +12,16 @@ import math
 
 from . import _lib
 from ._lib import (DIT_ATTN_BF16, DIT_ATTN_EDEVICE, DIT_ATTN_EINVAL, DIT_ATTN_ELAUNCH, DIT_ATTN_FP8_E4M3,
-                   DIT_ATTN_OK, DIT_ATTN_SPARSE_KV_BLOCK, DIT_ATTN_SPARSE_Q_BLOCK, DIT_ATTN_EUNSUPPORTED,
-                   dit_attn_fwd, dit_attn_fwd_blocksparse, dit_attn_fwd_ex, dit_attn_fwd_strided,
-                   dit_attn_quantize_e4m3, dit_attn_strerror, dit_attn_version)
+                   DIT_ATTN_MX_ALONG_D, DIT_ATTN_MX_ALONG_TOKENS, DIT_ATTN_OK, DIT_ATTN_SPARSE_KV_BLOCK,
+                   DIT_ATTN_SPARSE_Q_BLOCK, DIT_ATTN_EUNSUPPORTED, dit_attn_fwd, dit_attn_fwd_blocksparse,
+                   dit_attn_fwd_ex, dit_attn_fwd_mx, dit_attn_fwd_strided, dit_attn_quantize_e4m3,
+                   dit_attn_quantize_mx, dit_attn_strerror, dit_attn_version)
 
 __all__ = [
     "DitAttnError", "attention", "attention_blocksparse", "quantize_e4m3", "dit_attn_fwd", "dit_attn_fwd_ex",
     "dit_attn_fwd_strided", "dit_attn_fwd_blocksparse", "dit_attn_quantize_e4m3", "DIT_ATTN_SPARSE_Q_BLOCK",
-    "DIT_ATTN_SPARSE_KV_BLOCK",
+    "DIT_ATTN_SPARSE_KV_BLOCK", "attention_mx", "quantize_mx", "dit_attn_fwd_mx", "dit_attn_quantize_mx",
+    "DIT_ATTN_MX_ALONG_D", "DIT_ATTN_MX_ALONG_TOKENS",
     "dit_attn_strerror", "dit_attn_version", "DIT_ATTN_BF16", "DIT_ATTN_FP8_E4M3", "DIT_ATTN_OK",
     "DIT_ATTN_EINVAL", "DIT_ATTN_EUNSUPPORTED", "DIT_ATTN_EDEVICE", "DIT_ATTN_ELAUNCH",
 ]
@@ -123,6 +125,62 @@ def attention_blocksparse(q, k, v, kv_blocks, kv_counts, scale: float | None = N
                                   _stream_handle(stream))
     if st != DIT_ATTN_OK:
         raise DitAttnError(st, "dit_attn_fwd_blocksparse")
+    return out
+
+
+def quantize_mx(x, along: str, *, out=None, scales=None, stream=None):
+    """Block-scaled e4m3 quantisation of a contiguous bf16 (B, H, N, d) device tensor.
+
+    ``along`` is "d" (Q, K: scales (B, H, N, d/32)) or "tokens" (V: scales
+    (B, H, ceil(N/32), 32, d/32)); returns (codes float8_e4m3fn, scales uint8)."""
+    import torch
+    if x.dim() != 4 or x.dtype != torch.bfloat16 or not x.is_cuda or not x.is_contiguous():
+        raise ValueError("x must be a contiguous bf16 (B, H, N, d) device tensor")
+    B, H, N, d = x.shape
+    if along == "d":
+        ax, shape = DIT_ATTN_MX_ALONG_D, (B, H, N, d // 32)
+    elif along == "tokens":
+        ax, shape = DIT_ATTN_MX_ALONG_TOKENS, (B, H, -(-N // 32), 32, d // 32)
+    else:
+        raise ValueError('along must be "d" or "tokens"')
+    if out is None:
+        out = torch.empty(x.shape, dtype=torch.float8_e4m3fn, device=x.device)
+    if scales is None:
+        scales = torch.empty(shape, dtype=torch.uint8, device=x.device)
+    st = dit_attn_quantize_mx(x, B, H, N, d, ax, out, scales, _stream_handle(stream))
+    if st != DIT_ATTN_OK:
+        raise DitAttnError(st, "dit_attn_quantize_mx")
+    return out, scales
+
+
+def attention_mx(q8, q_scales, k8, k_scales, v8, v_scales, scale: float | None = None, *, out=None, lse=None,
+                 stream=None):
+    """Attention on block-scaled e4m3 inputs from ``quantize_mx`` (q, k along d, v along the tokens).
+
+    Contiguous float8_e4m3fn (B, H, N, 128) device tensors; returns bf16 O."""
+    import torch
+    if q8.dim() != 4 or k8.shape != q8.shape or v8.shape != q8.shape:
+        raise ValueError("q8, k8, v8 must share one (B, H, N, d) shape")
+    for t in (q8, k8, v8):
+        if t.dtype != torch.float8_e4m3fn or not t.is_cuda or not t.is_contiguous():
+            raise ValueError("q8, k8, v8 must be contiguous float8_e4m3fn device tensors")
+    B, H, N, d = q8.shape
+    for t, shape in ((q_scales, (B, H, N, d // 32)), (k_scales, (B, H, N, d // 32)),
+                     (v_scales, (B, H, -(-N // 32), 32, d // 32))):
+        if tuple(t.shape) != shape or t.dtype != torch.uint8 or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"scales must be contiguous uint8 device tensors of shape {shape}")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=q8.device)
+    elif out.shape != q8.shape or out.dtype != torch.bfloat16 or not out.is_cuda or not out.is_contiguous():
+        raise ValueError("out must be a contiguous bf16 device tensor of q8's shape")
+    if lse is not None and (lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous()):
+        raise ValueError("lse must be a contiguous float32 (B, H, N) tensor")
+    st = dit_attn_fwd_mx(q8, k8, v8, q_scales, k_scales, v_scales, out, B, H, N, d, float(scale), lse,
+                         _stream_handle(stream))
+    if st != DIT_ATTN_OK:
+        raise DitAttnError(st, "dit_attn_fwd_mx")
     return out
 
 

@@ -21,9 +21,11 @@ DIT_ATTN_ELAUNCH = -4
 
 DIT_ATTN_SPARSE_Q_BLOCK = 256
 DIT_ATTN_SPARSE_KV_BLOCK = 64
+DIT_ATTN_MX_ALONG_D = 0
+DIT_ATTN_MX_ALONG_TOKENS = 1
 
-EXPORTED = ("dit_attn_fwd", "dit_attn_fwd_blocksparse", "dit_attn_fwd_ex", "dit_attn_fwd_strided",
-            "dit_attn_quantize_e4m3", "dit_attn_strerror", "dit_attn_version")
+EXPORTED = ("dit_attn_fwd", "dit_attn_fwd_blocksparse", "dit_attn_fwd_ex", "dit_attn_fwd_mx", "dit_attn_fwd_strided",
+            "dit_attn_quantize_e4m3", "dit_attn_quantize_mx", "dit_attn_strerror", "dit_attn_version")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is not built; run `python -m diffusion_transformer_attention_non_amd.build` "
@@ -40,6 +42,10 @@ _lib.dit_attn_fwd_strided.restype = _i
 _lib.dit_attn_fwd_blocksparse.argtypes = [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _vp, _vp, _i,
                                           _vp, _vp, _vp, _vp]
 _lib.dit_attn_fwd_blocksparse.restype = _i
+_lib.dit_attn_fwd_mx.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _vp, _vp]
+_lib.dit_attn_fwd_mx.restype = _i
+_lib.dit_attn_quantize_mx.argtypes = [_vp, _i, _i, _i, _i, _i, _vp, _vp, _vp]
+_lib.dit_attn_quantize_mx.restype = _i
 _lib.dit_attn_quantize_e4m3.argtypes = [_vp, _i64, _vp, _vp, _vp, _vp]
 _lib.dit_attn_quantize_e4m3.restype = _i
 _lib.dit_attn_strerror.argtypes = [_i]
@@ -89,6 +95,15 @@ def dit_attn_fwd_blocksparse(q, k, v, o, B, H, N, d, scale, dtype, kv_blocks, kv
     return _lib.dit_attn_fwd_blocksparse(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, H, N, d, scale, dtype,
                                          _ptr(kv_blocks), _ptr(kv_counts), max_blocks, qp, op, _ptr(lse),
                                          _ptr(stream))
+
+
+def dit_attn_fwd_mx(q8, k8, v8, q_scales, k_scales, v_scales, o, B, H, N, d, scale, lse=None, stream=None) -> int:
+    return _lib.dit_attn_fwd_mx(_ptr(q8), _ptr(k8), _ptr(v8), _ptr(q_scales), _ptr(k_scales), _ptr(v_scales), _ptr(o),
+                                B, H, N, d, scale, _ptr(lse), _ptr(stream))
+
+
+def dit_attn_quantize_mx(x, B, H, N, d, along, x8, scales, stream=None) -> int:
+    return _lib.dit_attn_quantize_mx(_ptr(x), B, H, N, d, along, _ptr(x8), _ptr(scales), _ptr(stream))
 
 
 def dit_attn_quantize_e4m3(x, n, x8, descale, amax_ws, stream=None) -> int:

@@ -65,24 +65,114 @@ constexpr float kFp8PipePLog2 = 1.0f;          // P is scaled by 2 before the ca
 // O^T += V^T P^T with the accumulator held in AGPRs. The builtin form would keep
 // it in VGPRs, where its 128 registers per lane push the logits out to AGPR
 // copies. The compiler does not model this instruction's latency: the
-// accumulator's AGPRs are read by the VALU only after pv_drain() or after a
+// accumulator's AGPRs are read by the VALU only after pv_drain(...) or after a
 // full phase of other work, and its VGPR sources are not rewritten for a
 // whole sub-iteration after issue.
 __device__ __forceinline__ void pv_mfma(f32x16_t& acc, const i32x8_t& v, const i32x8_t& p) {
   asm("v_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, %0" : "+a"(acc) : "v"(v), "v"(p));
 }
-// 32 wait states: more than a 16-pass MFMA needs before its result is read
-__device__ __forceinline__ void pv_drain() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory"); }
+// 32 wait states: more than a 16-pass MFMA needs before its result is read.
+// The accumulators pass through it ("+a") and the products' sources are its
+// inputs: otherwise the compiler may hoist it above the (non-volatile)
+// products, read an accumulator right after the product that writes it, or
+// reuse a source register while the product still runs.
+__device__ __forceinline__ void pv_drain(f32x16_t (&acc)[2][4], const i32x8_t (&vf)[4], const i32x8_t (&p)[2],
+                                         int sv, int sp) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7"
+               : "+a"(acc[0][0]), "+a"(acc[0][1]), "+a"(acc[0][2]), "+a"(acc[0][3]), "+a"(acc[1][0]),
+                 "+a"(acc[1][1]), "+a"(acc[1][2]), "+a"(acc[1][3])
+               : "v"(vf[0]), "v"(vf[1]), "v"(vf[2]), "v"(vf[3]), "v"(p[0]), "v"(p[1]), "v"(sv), "v"(sp)
+               : "memory");
+}
+
+// Block scales of the MX form, E8M0 bytes (value 2^(byte - 127)). q and k:
+// one 32-bit word per row, byte j = d block j (d = 32 j .. 32 j + 31). v:
+// [B*H][ceil(N/32)][32] words per 32-token block, byte j of word i = column
+// 32 j + i.
+struct MxScales {
+  const uint8_t* q;
+  const uint8_t* k;
+  const uint8_t* v;
+};
+
+// The scaled 32x32x64 e4m3 MFMA. Lane l supplies one scale word per operand;
+// byte OA (OB) of it scales row (column) l % 32 over k-block l / 32, and
+// k-block b is bytes 16 b .. 16 b + 15 of the operand in both lane halves
+// (k = 16 h + 0..15 in half h's bytes 0-15, 32 + 16 h + 0..15 in bytes 16-31).
+template <int OA, int OB>
+__device__ __forceinline__ f32x16_t mfma_mx_t(const i32x8_t& a, const i32x8_t& b, const f32x16_t& c, int sa, int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, OA, sa, OB, sb);
+}
+// oa, ob are constants once the caller's loops are unrolled
+__device__ __forceinline__ f32x16_t mfma_mx(const i32x8_t& a, const i32x8_t& b, const f32x16_t& c, int sa, int oa,
+                                            int sb, int ob) {
+  switch (oa * 4 + ob) {
+#define DIT_MX_CASE(A, B) \
+  case A * 4 + B:         \
+    return mfma_mx_t<A, B>(a, b, c, sa, sb);
+    DIT_MX_CASE(0, 0) DIT_MX_CASE(0, 1) DIT_MX_CASE(0, 2) DIT_MX_CASE(0, 3)
+    DIT_MX_CASE(1, 0) DIT_MX_CASE(1, 1) DIT_MX_CASE(1, 2) DIT_MX_CASE(1, 3)
+    DIT_MX_CASE(2, 0) DIT_MX_CASE(2, 1) DIT_MX_CASE(2, 2) DIT_MX_CASE(2, 3)
+    DIT_MX_CASE(3, 0) DIT_MX_CASE(3, 1) DIT_MX_CASE(3, 2) default: return mfma_mx_t<3, 3>(a, b, c, sa, sb);
+#undef DIT_MX_CASE
+  }
+}
+// DMA instruction 4 of a K tile in the MX form: waves 0 and 1 (b32 == 0) move
+// K rows (16 bytes per lane); waves 2 and 3 move the tile's K scale words, 4
+// bytes per lane to M0 + 4 lane, so that the range check at the end of the
+// scale array works per word (a 16-byte chunk that straddles the end comes
+// back as zeros). The instruction is chosen inside one asm block: b32 is
+// uniform, and a branch in the C++ would split the scheduling region.
+__device__ __forceinline__ void dma_k4_mx(i32x4_t rsrc, int voffset, unsigned lds_addr, int b32) {
+  asm volatile(
+      "s_cmp_eq_u32 %3, 0\n\t"
+      "s_cbranch_scc1 1f\n\t"
+      "buffer_load_dword %0, %1, 0 offen lds\n\t"
+      "s_branch 2f\n"
+      "1:\n\t"
+      "buffer_load_dwordx4 %0, %1, 0 offen lds\n"
+      "2:" ::"v"(voffset), "s"(rsrc), "{m0}"(lds_addr), "s"(b32)
+      : "memory", "scc");
+}
+
+// pv_mfma with block scales: byte oa of sv for V^T, byte 0 of sp for P^T
+__device__ __forceinline__ void pv_mfma_mx(f32x16_t& acc, const i32x8_t& v, const i32x8_t& p, int sv, int sp,
+                                           int oa) {
+  switch (oa) {
+    case 0:
+      asm("v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel_hi:[0,0,0]"
+          : "+a"(acc) : "v"(v), "v"(p), "v"(sv), "v"(sp));
+      break;
+    case 1:
+      asm("v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel:[1,0,0] op_sel_hi:[0,0,0]"
+          : "+a"(acc) : "v"(v), "v"(p), "v"(sv), "v"(sp));
+      break;
+    case 2:
+      asm("v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel_hi:[1,0,0]"
+          : "+a"(acc) : "v"(v), "v"(p), "v"(sv), "v"(sp));
+      break;
+    default:
+      asm("v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel:[1,0,0] op_sel_hi:[1,0,0]"
+          : "+a"(acc) : "v"(v), "v"(p), "v"(sv), "v"(sp));
+      break;
+  }
+}
 
 // EXACT_LSE: the caller wants the log-sum-exp; it is then summed from the
 // unrounded fp32 probabilities as well (the output is normalised by the sums
 // of the e4m3 values in both forms).
-template <class C, bool EXACT_LSE>
+// MX: block-scaled inputs (scales in mxs, descale unused). Q and K fragments
+// then hold d in the MFMA's k order (so that each k-block is one 32-wide d
+// block), K scales ride in the K slot past the rows (in place of the two DMA
+// instructions that would only zero-fill there) and V scales in a fifth V
+// DMA instruction; both products use the scaled MFMA.
+template <class C, bool EXACT_LSE, bool MX = false>
 __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void attn_fwd_fp8_pipe_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __restrict__ Kg,
                               const uint8_t* __restrict__ Vg, uint16_t* __restrict__ Og,
                               float* __restrict__ LSEg, const float* __restrict__ descale,
-                              int N, int n_qtiles, float scale_log2, float scale, PipeSplit split, Layout L) {
+                              int N, int n_qtiles, float scale_log2, float scale, PipeSplit split, Layout L,
+                              MxScales mxs = MxScales{nullptr, nullptr, nullptr}) {
   constexpr int D = C::kD, KROW = C::kKRow;
   extern __shared__ __attribute__((aligned(16))) char smem[];
 
@@ -116,7 +206,8 @@ void attn_fwd_fp8_pipe_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __r
   const int l32 = lane & 31, hh = lane >> 5;
   const int q0 = qt * C::kBR + wave * 64;
 
-  // Q^T fragments: query q0 + qb*32 + l32, d = ks*64 + hh*32 .. +31
+  // Q^T fragments: query q0 + qb*32 + l32, d = ks*64 + hh*32 .. +31 (MX:
+  // d = ks*64 + hh*16 .. +15 and ks*64 + 32 + hh*16 .. +15, the MFMA's k order)
   i32x8_t qf[2][2];
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
@@ -125,12 +216,25 @@ void attn_fwd_fp8_pipe_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __r
     for (int ks = 0; ks < 2; ++ks) {
       i32x4_t a = {0, 0, 0, 0}, b = {0, 0, 0, 0};
       if (row < N) {
-        const uint8_t* p = Qg + ibase + (long long)row * L.qn + ks * 64 + hh * 32;
-        a = *(const i32x4_t*)p;
-        b = *(const i32x4_t*)(p + 16);
+        const uint8_t* p = Qg + ibase + (long long)row * L.qn + ks * 64;
+        a = *(const i32x4_t*)(p + (MX ? hh * 16 : hh * 32));
+        b = *(const i32x4_t*)(p + (MX ? 32 + hh * 16 : hh * 32 + 16));
       }
       qf[qb][ks] = i32x8_t{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
     }
+  }
+  // MX scale words of this lane: byte 2 x + ks = row block x (query block or
+  // key block), d block 2 ks + hh; v_perm picks those bytes of two row words
+  const int sc_sel = hh ? 0x07050301 : 0x06040200;
+  int qsc = 0;
+  if constexpr (MX) {
+    int w[2];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      const int row = q0 + qb * 32 + l32;
+      w[qb] = row < N ? *(const int*)(mxs.q + ((size_t)bh * N + row) * 4) : 0;
+    }
+    qsc = __builtin_amdgcn_perm(w[1], w[0], sc_sel);
   }
 
   // ---- DMA lane offsets: instruction i writes LDS bytes [1024 i, 1024 i + 1024)
@@ -155,10 +259,41 @@ void attn_fwd_fp8_pipe_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __r
     rs[3] = 0x00020000;
     return rs;
   };
+  // MX: instruction 4 of waves 2 and 3 (LDS bytes 18432.. and 19456.. of a K
+  // slot) carries the tile's K scale words of keys 0-63 and 64-127, that of
+  // every wave (16384.. of a V slot) its four V scale blocks; lanes past the
+  // data zero-fill
+  auto bytes_rsrc = [&](const uint8_t* base, long long off, int bytes) __attribute__((always_inline)) {
+    const unsigned long long a = (unsigned long long)(base + off);
+    i32x4_t rs;
+    rs[0] = __builtin_amdgcn_readfirstlane((int)(unsigned)a);
+    rs[1] = __builtin_amdgcn_readfirstlane((int)((a >> 32) & 0xffffu));
+    rs[2] = __builtin_amdgcn_readfirstlane(max(bytes, 0));
+    rs[3] = 0x00020000;
+    return rs;
+  };
+  const int n_vb = (N + 31) / 32;
+  auto kscale_rsrc = [&](int t) __attribute__((always_inline)) {
+    return bytes_rsrc(mxs.k, ((long long)bh * N + (long long)t * C::kTileKeys) * 4,
+                      min(C::kTileKeys, N - t * C::kTileKeys) * 4);
+  };
+  auto vscale_rsrc = [&](int t) __attribute__((always_inline)) {
+    return bytes_rsrc(mxs.v, ((long long)bh * n_vb + (long long)t * 4) * 128, min(4, n_vb - t * 4) * 128);
+  };
+  if constexpr (MX) {
+    static_assert(C::kKTile == 18 * 1024 && C::kVTile == 16 * 1024, "scale DMAs land past the tile rows");
+    if (wave >= 2) kdo[4] = (wave - 2) * 256 + lane * 4;
+    vdo[4] = wave * 1024 + lane * 16;
+  }
   auto dma_one = [&](const i32x4_t& rs, const char* slot, const int (&off)[C::kDmaPerWave], int m)
       __attribute__((always_inline)) {
     const int i = wave + 4 * m;
     dma_b128(rs, off[m], __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)DIT_LDS(const char, slot) + i * 1024));
+  };
+  auto dma_k4 = [&](const i32x4_t& rs, const char* slot) __attribute__((always_inline)) {
+    const int i = wave + 16;
+    dma_k4_mx(rs, kdo[4], __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)DIT_LDS(const char, slot) + i * 1024),
+              __builtin_amdgcn_readfirstlane(wave >= 2 ? 1 : 0));
   };
   auto dma_tile = [&](const char* head, int t, const char* slot, const int (&off)[C::kDmaPerWave])
       __attribute__((always_inline)) {
@@ -172,8 +307,9 @@ void attn_fwd_fp8_pipe_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __r
   };
 
   // ---- fragment reads
-  const int k_rd = l32 * KROW + hh * 32;
+  const int k_rd = l32 * KROW + (MX ? hh * 16 : hh * 32);
   i32x8_t kf[2][2];                                     // [key block][d step]
+  int ksc = 0;                                          // MX: the K scale word (bytes as qsc's)
   auto read_kfrags = [&](int j) {
     const char* kb = kslot(j >> 1) + (j & 1) * 64 * KROW + k_rd;
 #pragma unroll
@@ -181,9 +317,13 @@ void attn_fwd_fp8_pipe_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __r
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         const i32x4_t a0 = *(const i32x4_t*)(kb + b * 32 * KROW + ks * 64);
-        const i32x4_t a1 = *(const i32x4_t*)(kb + b * 32 * KROW + ks * 64 + 16);
+        const i32x4_t a1 = *(const i32x4_t*)(kb + b * 32 * KROW + ks * 64 + (MX ? 32 : 16));
         kf[b][ks] = i32x8_t{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
       }
+    if constexpr (MX) {
+      const char* sb = kslot(j >> 1) + C::kKTile + (j & 1) * 1024 + l32 * 4;
+      ksc = __builtin_amdgcn_perm(*(const int*)(sb + 128), *(const int*)sb, sc_sel);
+    }
   };
   // V^T gather (the key order of the P^T packing): lane pair gi>>1 addresses key
   // slot tr_e of an 8-key read; the XOR of the V swizzle depends on key bits
@@ -196,8 +336,12 @@ void attn_fwd_fp8_pipe_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __r
 #pragma unroll
   for (int db = 0; db < 4; ++db) v_rd[db] = tr_key * 128 + (((2 * db) ^ tr_gk) + (g & 1)) * 16 + (gi & 1) * 8;
   i32x8_t vf[4];                                        // [d block]
+  int vsc = 0;                                          // MX: V scale word, byte db = column 32 db + l32
   auto read_vfrags = [&](int j, int half) {             // half 0: d blocks 0, 1; half 1: 2, 3
     const char* vb = vslot(j >> 1) + (j & 1) * 64 * 128;
+    if constexpr (MX) {
+      if (half == 0) vsc = *(const int*)(vslot(j >> 1) + C::kVTile + ((j & 1) * 2 + hh) * 128 + l32 * 4);
+    }
 #pragma unroll
     for (int db = half * 2; db < half * 2 + 2; ++db) {
       // one lane address per d block; the four reads then differ by constants,
@@ -229,8 +373,12 @@ void attn_fwd_fp8_pipe_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __r
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[b][r] = 0.f;
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-        s[b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kf[b][ks], qf[qb][ks], s[b], 0, 0, 0, 0, 0, 0);
+      for (int ks = 0; ks < 2; ++ks) {
+        if constexpr (MX)
+          s[b] = mfma_mx(kf[b][ks], qf[qb][ks], s[b], ksc, 2 * b + ks, qsc, 2 * qb + ks);
+        else
+          s[b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kf[b][ks], qf[qb][ks], s[b], 0, 0, 0, 0, 0, 0);
+      }
     }
   };
   auto row_max = [&](const f32x16_t (&s)[2]) {
@@ -260,6 +408,7 @@ void attn_fwd_fp8_pipe_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __r
   // A holds ones exactly where row r meets k-group r, so output row r, column
   // c is the sum of the 32 values in lane 16 r + c. Lanes 0..15 receive rows
   // 0..3: the half-row sums of queries c (rows 0, 2) and c + 16 (rows 1, 3).
+  const int p_one = 0x7F7F7F7F;          // MX: scale 2^0 for P^T
   const int ones_w = (lane & 15) == (lane >> 4) ? 0x38383838 : 0;   // e4m3 1.0
   const i32x8_t ones = {ones_w, ones_w, ones_w, ones_w, ones_w, ones_w, ones_w, ones_w};
   auto psum = [&](const i32x8_t& pt) __attribute__((always_inline)) {
@@ -282,11 +431,31 @@ void attn_fwd_fp8_pipe_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __r
   i32x8_t pA[2], pB[2];               // P^T of two consecutive sub-tiles [query block]
 
   // ---- prologue: K tiles u0..u0+2, V tiles u0, u0+1; the first sub-tile's logits
-  dma_tile(Kh, u0, kslot(u0), kdo);
-  if (u0 + 1 < u1) dma_tile(Kh, u0 + 1, kslot(u0 + 1), kdo);
-  if (u0 + 2 < u1) dma_tile(Kh, u0 + 2, kslot(u0 + 2), kdo);
-  dma_tile(Vh, u0, vslot(u0), vdo);
-  if (u0 + 1 < u1) dma_tile(Vh, u0 + 1, vslot(u0 + 1), vdo);
+  auto dma_ktile = [&](int t) __attribute__((always_inline)) {
+    if constexpr (MX) {
+      const i32x4_t rs = tile_rsrc(Kh, t);
+#pragma unroll
+      for (int m = 0; m < 4; ++m) dma_one(rs, kslot(t), kdo, m);
+      dma_k4(wave >= 2 ? kscale_rsrc(t) : rs, kslot(t));
+    } else {
+      dma_tile(Kh, t, kslot(t), kdo);
+    }
+  };
+  auto dma_vtile = [&](int t) __attribute__((always_inline)) {
+    if constexpr (MX) {
+      const i32x4_t rs = tile_rsrc(Vh, t);
+#pragma unroll
+      for (int m = 0; m < 4; ++m) dma_one(rs, vslot(t), vdo, m);
+      dma_one(vscale_rsrc(t), vslot(t), vdo, 4);
+    } else {
+      dma_tile(Vh, t, vslot(t), vdo);
+    }
+  };
+  dma_ktile(u0);
+  if (u0 + 1 < u1) dma_ktile(u0 + 1);
+  if (u0 + 2 < u1) dma_ktile(u0 + 2);
+  dma_vtile(u0);
+  if (u0 + 1 < u1) dma_vtile(u0 + 1);
   __builtin_amdgcn_s_waitcnt(0x0F70);      // vmcnt(0)
   __syncthreads();
   read_kfrags(2 * u0);
@@ -316,7 +485,10 @@ void attn_fwd_fp8_pipe_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __r
 #pragma unroll
       for (int st = 0; st < 8; ++st) {
         const int db = st >> 1, qb = st & 1;
-        pv_mfma(acc[qb][db], vf[db], pin[qb]);
+        if constexpr (MX)
+          pv_mfma_mx(acc[qb][db], vf[db], pin[qb], vsc, p_one, db);
+        else
+          pv_mfma(acc[qb][db], vf[db], pin[qb]);
         soft_step(s0, st, nm0, pout[0], ls0);
         DIT_FENCE();
       }
@@ -329,7 +501,10 @@ void attn_fwd_fp8_pipe_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __r
 #pragma unroll
           for (int r = 0; r < 16; ++r) dst[r] = 0.f;
         }
-        dst = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kf[b][ks], qf[qb][ks], dst, 0, 0, 0, 0, 0, 0);
+        if constexpr (MX)
+          dst = mfma_mx(kf[b][ks], qf[qb][ks], dst, ksc, 2 * b + ks, qsc, 2 * qb + ks);
+        else
+          dst = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kf[b][ks], qf[qb][ks], dst, 0, 0, 0, 0, 0, 0);
       };
 #pragma unroll
       for (int st = 0; st < 8; ++st) {
@@ -436,6 +611,11 @@ void attn_fwd_fp8_pipe_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __r
     constexpr bool TAIL = decltype(tail_c)::value;
     const bool k_next = !TAIL || u + 3 < u1, v_next = !TAIL || u + 2 < u1;
     const i32x4_t rk = tile_rsrc(Kh, u + 3), rv = tile_rsrc(Vh, u + 2);
+    i32x4_t rk4 = rk, rvs = rv;          // MX: the scale instructions' sources
+    if constexpr (MX) {
+      rk4 = wave >= 2 ? kscale_rsrc(u + 3) : rk;
+      rvs = vscale_rsrc(u + 2);
+    }
     const char* sk = kslot(u + 3);
     const char* sv = vslot(u + 2);
     DIT_FENCE();
@@ -443,17 +623,27 @@ void attn_fwd_fp8_pipe_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __r
     sub(2 * u, pA, pB, tail_c, [&](int st) __attribute__((always_inline)) {
       if (k_next) {
         dma_one(rk, sk, kdo, st);
-        if (st == 0) dma_one(rk, sk, kdo, 4);
+        if (st == 0) {
+          if constexpr (MX)
+            dma_k4(rk4, sk);
+          else
+            dma_one(rk, sk, kdo, 4);
+        }
       }
     });
     sub(2 * u + 1, pB, pA, tail_c, [&](int st) __attribute__((always_inline)) {
       // a V tile is 16 KB: instructions 16-19 (m = 4) would only zero-fill
-      // rows that are never read
-      if (v_next) dma_one(rv, sv, vdo, st);
+      // rows that are never read; the MX form sends its scales with them
+      if (v_next) {
+        dma_one(rv, sv, vdo, st);
+        if (MX && st == 0) dma_one(rvs, sv, vdo, 4);
+      }
     });
     DIT_FENCE();
     if (TAIL)
       __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    else if (MX)
+      __builtin_amdgcn_s_waitcnt(0x0F7A);  // vmcnt(10): 5 K and 5 V instructions may stay in flight
     else
       __builtin_amdgcn_s_waitcnt(0x0F79);  // vmcnt(9): this iteration's 9 DMAs (5 K, 4 V) may stay in flight
     __syncthreads();
@@ -467,9 +657,13 @@ void attn_fwd_fp8_pipe_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __r
 #pragma unroll
   for (int db = 0; db < 4; ++db)
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
-      pv_mfma(acc[qb][db], vf[db], pA[qb]);
-  pv_drain();
+    for (int qb = 0; qb < 2; ++qb) {
+      if constexpr (MX)
+        pv_mfma_mx(acc[qb][db], vf[db], pA[qb], vsc, p_one, db);
+      else
+        pv_mfma(acc[qb][db], vf[db], pA[qb]);
+    }
+  pv_drain(acc, vf, pA, vsc, p_one);
 
   // l sums 8 p, and so does acc: their ratio needs no further scaling
   float l_q[2];                        // the row sum of this lane's query

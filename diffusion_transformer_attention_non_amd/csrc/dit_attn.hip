@@ -13,6 +13,7 @@
 #include "attn_fwd_bf16_pipe.h"
 #include "attn_fwd_fp8_pipe.h"
 #include "quant_e4m3.h"
+#include "quant_mx.h"
 
 using namespace ditattn;
 
@@ -46,11 +47,15 @@ hipError_t allow_lds_pipe() {
 }
 template <class C>
 hipError_t allow_lds_fp8() {
-  const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_fwd_fp8_pipe_kernel<C, false>),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, C::kLdsBytes);
-  if (e != hipSuccess) return e;
-  return hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_fwd_fp8_pipe_kernel<C, true>),
-                             hipFuncAttributeMaxDynamicSharedMemorySize, C::kLdsBytes);
+  const void* kernels[4] = {reinterpret_cast<const void*>(&attn_fwd_fp8_pipe_kernel<C, false, false>),
+                            reinterpret_cast<const void*>(&attn_fwd_fp8_pipe_kernel<C, true, false>),
+                            reinterpret_cast<const void*>(&attn_fwd_fp8_pipe_kernel<C, false, true>),
+                            reinterpret_cast<const void*>(&attn_fwd_fp8_pipe_kernel<C, true, true>)};
+  for (const void* k : kernels) {
+    const hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, C::kLdsBytes);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 int check_device() {
@@ -209,9 +214,11 @@ int launch_pipe(const void* q, const void* k, const void* v, void* o, float* lse
   return err == hipSuccess ? DIT_ATTN_OK : DIT_ATTN_ELAUNCH;
 }
 
-template <class C>
+// MX: block-scaled inputs with their scales in mxs (descale unused)
+template <class C, bool MX = false>
 int launch_fp8(const void* q, const void* k, const void* v, void* o, float* lse, const float* descale,
-               int BH, int N, float scale, hipStream_t st, int n_cu, const Layout& L) {
+               int BH, int N, float scale, hipStream_t st, int n_cu, const Layout& L,
+               const MxScales& mxs = MxScales{nullptr, nullptr, nullptr}) {
   const int n_qtiles = (N + C::kBR - 1) / C::kBR;
   const long long tiles = (long long)n_qtiles * BH;
   if (tiles > 0x7fffffffLL / 8) return DIT_ATTN_EINVAL;
@@ -234,11 +241,11 @@ int launch_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
     }
   }
   const long long grid = (long long)sp.n_full + (long long)sp.n_split * sp.parts;
-  auto* kernel = lse != nullptr ? &attn_fwd_fp8_pipe_kernel<C, true> : &attn_fwd_fp8_pipe_kernel<C, false>;
+  auto* kernel = lse != nullptr ? &attn_fwd_fp8_pipe_kernel<C, true, MX> : &attn_fwd_fp8_pipe_kernel<C, false, MX>;
   hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(C::kThreads), C::kLdsBytes, st,
                      static_cast<const uint8_t*>(q), static_cast<const uint8_t*>(k),
                      static_cast<const uint8_t*>(v), static_cast<uint16_t*>(o), lse, descale, N, n_qtiles,
-                     scale_log2, scale, sp, L);
+                     scale_log2, scale, sp, L, mxs);
   hipError_t err = hipGetLastError();
   if (ws != nullptr) {
     if (err == hipSuccess) {
@@ -303,7 +310,7 @@ int check_call(const void* q, const void* k, const void* v, void* o, int B, int 
 
 extern "C" {
 
-int dit_attn_version(void) { return (1 << 16) | 2; }
+int dit_attn_version(void) { return (1 << 16) | 3; }
 
 const char* dit_attn_strerror(int status) {
   switch (status) {
@@ -369,6 +376,62 @@ int dit_attn_fwd_ex(const void* q, const void* k, const void* v, void* o, int B,
 int dit_attn_fwd(const void* q, const void* k, const void* v, void* o, int B, int H, int N, int d, float scale,
                  int dtype, void* stream) {
   return dit_attn_fwd_ex(q, k, v, o, B, H, N, d, scale, dtype, nullptr, nullptr, stream);
+}
+
+int dit_attn_fwd_mx(const void* q8, const void* k8, const void* v8, const void* q_scales, const void* k_scales,
+                    const void* v_scales, void* o, int B, int H, int N, int d, float scale, float* lse, void* stream) {
+  Checked c;
+  const int status = check_call(q8, k8, v8, o, B, H, N, d, scale, DIT_ATTN_FP8_E4M3, nullptr, nullptr, nullptr, lse, &c);
+  if (status != DIT_ATTN_OK) return status;
+  if (!q_scales || !k_scales || !v_scales) return DIT_ATTN_EINVAL;
+  if (!aligned(q_scales, 16) || !aligned(k_scales, 16) || !aligned(v_scales, 16)) return DIT_ATTN_EINVAL;
+  const uint64_t row_scale_bytes = (uint64_t)c.bh * (uint64_t)N * 4u;
+  const uint64_t v_scale_bytes = (uint64_t)c.bh * (uint64_t)((N + 31) / 32) * 128u;
+  const void* sc[3] = {q_scales, k_scales, v_scales};
+  const uint64_t sb[3] = {row_scale_bytes, row_scale_bytes, v_scale_bytes};
+  for (int i = 0; i < 3; ++i) {
+    if (overlap(o, c.out_bytes, sc[i], sb[i])) return DIT_ATTN_EINVAL;
+    if (lse && overlap(lse, c.lse_bytes, sc[i], sb[i])) return DIT_ATTN_EINVAL;
+  }
+  const int dev_status = check_device();
+  if (dev_status != DIT_ATTN_OK) return dev_status;
+  const MxScales mxs{static_cast<const uint8_t*>(q_scales), static_cast<const uint8_t*>(k_scales),
+                     static_cast<const uint8_t*>(v_scales)};
+  return launch_fp8<CfgFp8D128, true>(q8, k8, v8, o, lse, nullptr, c.bh, N, scale, static_cast<hipStream_t>(stream),
+                                      cu_count(), c.L, mxs);
+}
+
+int dit_attn_quantize_mx(const void* x, int B, int H, int N, int d, int along, void* x8, void* scales,
+                         void* stream) {
+  if (!x || !x8 || !scales) return DIT_ATTN_EINVAL;
+  if (!aligned(x, 16) || !aligned(x8, 16)) return DIT_ATTN_EINVAL;
+  if (B < 1 || H < 1 || N < 1 || d < 32 || d % 32 != 0 || d > 1024) return DIT_ATTN_EINVAL;
+  if (along != DIT_ATTN_MX_ALONG_D && along != DIT_ATTN_MX_ALONG_TOKENS) return DIT_ATTN_EINVAL;
+  const long long bh = (long long)B * H;
+  if (bh > 65535) return DIT_ATTN_EINVAL;                 // grid y of the token-blocked kernel
+  const unsigned __int128 n = (unsigned __int128)bh * (unsigned)N * (unsigned)d;
+  if (n >= ((unsigned __int128)1 << 62)) return DIT_ATTN_EINVAL;
+  const uint64_t n_el = (uint64_t)n;
+  const uint64_t scale_bytes = along == DIT_ATTN_MX_ALONG_D ? n_el / 32
+                                                          : (uint64_t)bh * (uint64_t)((N + 31) / 32) * (uint64_t)d;
+  if (overlap(x, n_el * 2u, x8, n_el) || overlap(x, n_el * 2u, scales, scale_bytes) ||
+      overlap(x8, n_el, scales, scale_bytes))
+    return DIT_ATTN_EINVAL;
+  const int dev_status = check_device();
+  if (dev_status != DIT_ATTN_OK) return dev_status;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const uint16_t* xb = static_cast<const uint16_t*>(x);
+  if (along == DIT_ATTN_MX_ALONG_D) {
+    const int64_t n_blocks = (int64_t)(n_el / 32);
+    const int64_t want = (n_blocks + kQuantThreads - 1) / kQuantThreads;
+    const unsigned blocks = (unsigned)(want < 4096 ? want : 4096);
+    hipLaunchKernelGGL(quant_mx_rows_kernel, dim3(blocks), dim3(kQuantThreads), 0, st, xb, n_blocks,
+                       static_cast<uint8_t*>(x8), static_cast<uint8_t*>(scales));
+  } else {
+    hipLaunchKernelGGL(quant_mx_tokens_kernel, dim3((unsigned)((N + 31) / 32), (unsigned)bh), dim3(d), 0, st, xb, N,
+                       d, static_cast<uint8_t*>(x8), static_cast<uint8_t*>(scales));
+  }
+  return hipGetLastError() == hipSuccess ? DIT_ATTN_OK : DIT_ATTN_ELAUNCH;
 }
 
 int dit_attn_quantize_e4m3(const void* x, int64_t n, void* x8, float* descale, uint32_t* amax_ws,

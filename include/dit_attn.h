@@ -174,6 +174,60 @@ DIT_ATTN_API int dit_attn_fwd_blocksparse(const void* q, const void* k, const vo
                              const int64_t* qkv_strides, const int64_t* o_strides,
                              float* lse, void* stream);
 
+/* Block axis of dit_attn_quantize_mx. */
+#define DIT_ATTN_MX_ALONG_D 0       /* 32 consecutive d values of a row (Q, K) */
+#define DIT_ATTN_MX_ALONG_TOKENS 1  /* 32 consecutive tokens of a column (V) */
+
+/*
+ * dit_attn_fwd_mx - attention on block-scaled e4m3 inputs (MX style), with
+ * the scaled e4m3 matrix product of gfx950.
+ *
+ * The pages report fp8 attention variants (Japanese summary, third
+ * paragraph) without their scaling. Here every 32 consecutive values of an
+ * input share one power-of-two scale 2^e, held as the E8M0 byte e + 127:
+ * along d for q and k, along the tokens for v, so that each block lies in one
+ * 32-wide slice of the contraction it enters. Real values are code * 2^e;
+ * dit_attn_quantize_mx produces all three. The rest is the fp8 pipeline of
+ * dit_attn_fwd with DIT_ATTN_FP8_E4M3 (logits from the dequantised values
+ * times scale, P rounded to e4m3, O divided by the sum of the rounded P).
+ *
+ * q8, k8, v8 : device e4m3 codes, contiguous [B][H][N][d], 16-byte aligned.
+ * q_scales,
+ * k_scales   : device bytes [B][H][N][d/32]: byte j of row n scales d = 32 j
+ *              .. 32 j + 31. 16-byte aligned.
+ * v_scales   : device bytes [B][H][ceil(N/32)][32][d/32]: entry (t, i, j)
+ *              scales column 32 j + i over tokens 32 t .. 32 t + 31.
+ *              16-byte aligned.
+ * o, lse, B, H, N, scale, stream: as for dit_attn_fwd_ex. d must be 128
+ * (else DIT_ATTN_EUNSUPPORTED). o and lse must not overlap any input or
+ * scale array. Statuses as for dit_attn_fwd_ex.
+ */
+DIT_ATTN_API int dit_attn_fwd_mx(const void* q8, const void* k8, const void* v8,
+                    const void* q_scales, const void* k_scales, const void* v_scales, void* o,
+                    int B, int H, int N, int d, float scale, float* lse, void* stream);
+
+/*
+ * dit_attn_quantize_mx - block-scaled e4m3 quantisation of a bf16 tensor.
+ *
+ * x      : device bfloat16, contiguous [B][H][N][d], 16-byte aligned;
+ *          32 <= d <= 1024, d a multiple of 32; B*H <= 65535.
+ * along  : DIT_ATTN_MX_ALONG_D (scales [B][H][N][d/32]) or
+ *          DIT_ATTN_MX_ALONG_TOKENS (scales [B][H][ceil(N/32)][32][d/32], the
+ *          layouts dit_attn_fwd_mx reads).
+ * For each block of 32 values: amax = max |x|; e = the smallest integer with
+ * amax / 2^e <= 448, at least -127 (an all-zero block takes -127); the scale
+ * byte is e + 127; each code is the e4m3 value nearest to x / 2^e (ties to
+ * even). Nothing saturates. (The OCP Microscaling MXFP8 conversion takes
+ * e = floor(log2 amax) - 8 and clips the block maximum instead; this rule is
+ * one exponent step larger for blocks whose maximum's significand exceeds
+ * 1.75.)
+ * x8     : device uint8, same shape as x, 16-byte aligned; must not overlap x.
+ * scales : device uint8 array of the size above; must not overlap x or x8.
+ * Statuses: DIT_ATTN_EINVAL for bad pointers or sizes, _EDEVICE, _ELAUNCH.
+ */
+DIT_ATTN_API int dit_attn_quantize_mx(const void* x, int B, int H, int N, int d, int along, void* x8,
+                         void* scales, void* stream);
+
 /*
  * dit_attn_quantize_e4m3 - per-tensor absmax quantisation of a bf16 tensor.
  *
@@ -198,7 +252,7 @@ DIT_ATTN_API int dit_attn_quantize_e4m3(const void* x, int64_t n, void* x8, floa
 DIT_ATTN_API const char* dit_attn_strerror(int status);
 
 /* Library ABI version: (major << 16) | minor (1.1 adds dit_attn_fwd_strided,
-   1.2 dit_attn_fwd_blocksparse). */
+   1.2 dit_attn_fwd_blocksparse, 1.3 dit_attn_fwd_mx and dit_attn_quantize_mx). */
 DIT_ATTN_API int dit_attn_version(void);
 
 #ifdef __cplusplus

@@ -23,9 +23,9 @@ def lib():
 
 
 def test_header_declares_the_entry_points():
-    assert _declared() == sorted(["dit_attn_fwd", "dit_attn_fwd_blocksparse", "dit_attn_fwd_ex",
-                                  "dit_attn_fwd_strided", "dit_attn_quantize_e4m3", "dit_attn_strerror",
-                                  "dit_attn_version"])
+    assert _declared() == sorted(["dit_attn_fwd", "dit_attn_fwd_blocksparse", "dit_attn_fwd_ex", "dit_attn_fwd_mx",
+                                  "dit_attn_fwd_strided", "dit_attn_quantize_e4m3", "dit_attn_quantize_mx",
+                                  "dit_attn_strerror", "dit_attn_version"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -150,6 +150,45 @@ def test_blocksparse_list_overlapping_lse(lib):
     assert lib.dit_attn_fwd_blocksparse(*args, LB, LC, 16, None, None, lse, None) == -3
     assert lib.dit_attn_fwd_blocksparse(*args, lse + 4000, LC, 16, None, None, lse, None) == -1
     assert lib.dit_attn_fwd_blocksparse(*args, LB, lse + 8, 16, None, None, lse, None) == -1
+
+
+# MX: (B, H, N, d) = (1, 2, 100, 128); codes 25600 bytes, row scales 800, V scales 4 * 128 * 2 = 1024
+QS, KS, VS = 0x8000000, 0x9000000, 0xA000000
+
+
+@pytest.mark.parametrize("args,expect,why", [
+    ((SA, SB, SC, QS, KS, VS, SO, 1, 2, 100, 128, 0.1, None), -3, "valid (no GPU here: device error)"),
+    ((SA, SB, SC, 0, KS, VS, SO, 1, 2, 100, 128, 0.1, None), -1, "NULL q scales"),
+    ((SA, SB, SC, QS, KS + 4, VS, SO, 1, 2, 100, 128, 0.1, None), -1, "k scales not 16-byte aligned"),
+    ((SA, SB, SC, QS, KS, SO + 64, SO, 1, 2, 100, 128, 0.1, None), -1, "v scales overlap o"),
+    ((SA, SB, SC, QS, KS, VS, SO, 1, 2, 100, 64, 0.1, None), -2, "d = 64"),
+    ((SA, SB, SC, QS, KS, VS, SO, 1, 2, 100, 128, -1.0, None), -1, "negative scale"),
+    ((SA, SB, SC, QS, KS, VS, SA + 16, 1, 2, 100, 128, 0.1, None), -1, "o overlaps q8"),
+    ((SA, SB, SC, QS, KS, VS, SO, 1, 2, 100, 128, 0.1, QS + 400), -1, "lse overlaps q scales"),
+])
+def test_mx_attention_checks(lib, args, expect, why):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert lib.dit_attn_fwd_mx(*args) == expect, why
+
+
+@pytest.mark.parametrize("args,expect,why", [
+    ((SA, 1, 2, 100, 128, 0, SB, SC), -3, "along d (no GPU here: device error)"),
+    ((SA, 1, 2, 100, 128, 1, SB, SC), -3, "along tokens"),
+    ((SA, 1, 2, 100, 128, 2, SB, SC), -1, "unknown axis"),
+    ((SA, 1, 2, 100, 48, 0, SB, SC), -1, "d not a multiple of 32"),
+    ((SA, 1, 2, 100, 2048, 0, SB, SC), -1, "d above 1024"),
+    ((SA, 1, 2, 0, 128, 0, SB, SC), -1, "N = 0"),
+    ((SA, 1, 2, 100, 128, 0, SA + 64, SC), -1, "codes overlap x"),
+    ((SA, 1, 2, 100, 128, 0, SB, SB + 100), -1, "scales overlap codes"),
+    ((SA, 300, 300, 100, 128, 1, SB, SC), -1, "B H above the token kernel's grid"),
+])
+def test_mx_quantize_checks(lib, args, expect, why):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert lib.dit_attn_quantize_mx(*args, None) == expect, why
 
 
 def test_fwd_ex_rejects_bad_lse(lib):

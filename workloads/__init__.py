@@ -201,3 +201,22 @@ def random_kv_blocks(B, H, N, density, seed=0, *, q_block=256, kv_block=64, n_te
         counts[t] = x.size
     return (torch.from_numpy(blocks.reshape(B, H, nq, mb)).contiguous(),
             torch.from_numpy(counts.reshape(B, H, nq)).contiguous())
+
+
+def block_varied_qkv(B, H, N, d, seed=0, qk_range=2, v_range=6):
+    """Q, K, V whose 32-value blocks carry different powers of two: iid N(0,1)
+    values times 2^k, k uniform in [-qk_range, qk_range] per (row, 32 d values)
+    of Q and K and in [-v_range, v_range] per (32 tokens, column) of V. The
+    block-scaled formats give each such block its own scale, so inputs like
+    these tell apart the blocks that iid values (whose blocks all have about
+    the same maximum) would not."""
+    q, k, v = random_qkv(B, H, N, d, seed=seed)
+    rng = np.random.default_rng(seed + 1000)
+    def along_d(t, r):
+        ex = rng.integers(-r, r + 1, size=(B, H, N, d // 32))
+        f = torch.from_numpy(np.repeat(np.ldexp(1.0, ex), 32, axis=-1)).float()
+        return (t.float() * f).to(torch.bfloat16).contiguous()
+    nt = -(-N // 32)
+    ex = rng.integers(-v_range, v_range + 1, size=(B, H, nt, d))
+    fv = torch.from_numpy(np.repeat(np.ldexp(1.0, ex), 32, axis=2)[:, :, :N]).float()
+    return along_d(q, qk_range), along_d(k, qk_range), (v.float() * fv).to(torch.bfloat16).contiguous()
