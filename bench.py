@@ -10,9 +10,11 @@ uses the per-launch kernel time from events recorded on the stream the
 kernel runs on. ``cpu_baseline`` times the fp64 CPU oracle on a bounded
 sample of query rows of the same workload (each output row depends on one
 query row, so a row sample is the same computation, only fewer rows).
-``fp8`` and ``blocksparse`` are companion figures of the same workload: the
-e4m3 path, and block-sparse attention over the text key blocks plus a seeded
-fraction of the image key blocks (TFLOP/s over the keys actually visited).
+``fp8``, ``fp8_mx`` and ``blocksparse`` are companion figures of the same
+workload: the e4m3 path with per-tensor scales, the e4m3 path with one scale
+per 32 values (scaled MFMA), and block-sparse attention over the text key
+blocks plus a seeded fraction of the image key blocks (TFLOP/s over the keys
+actually visited).
 """
 from __future__ import annotations
 
@@ -218,6 +220,25 @@ def main(argv=None):
                                     "peak": PEAK_TFLOPS["fp8"], "unit": "TFLOP/s",
                                     "frac": round(flops / (k8_mean * 1e-3) / 1e12 / PEAK_TFLOPS["fp8"], 4),
                                     "traffic": load_traffic("attn_fwd_fp8", w.name)}}
+
+    if not args.no_fp8 and args.layout == "bhnd" and d == 128:
+        # block-scaled e4m3 (32-value blocks, E8M0 scales) on the scaled MFMA
+        (qm, qsc), (km, ksc) = dit.quantize_mx(qd, "d"), dit.quantize_mx(kd, "d")
+        vm, vsc = dit.quantize_mx(vd, "tokens")
+
+        def step_mx():
+            st = dit.dit_attn_fwd_mx(qm, km, vm, qsc, ksc, vsc, od, B, H, N, d, scale, None, handle)
+            if st != 0:
+                raise dit.DitAttnError(st, "dit_attn_fwd_mx")
+
+        wallm, perm = time_launches(step_mx, args.warmup, args.steps)
+        km_mean = statistics.fmean(perm)
+        line["fp8_mx"] = {"workload": w.name + "_mx", "value": round(flops / (wallm / args.steps) / 1e12, 2),
+                          "unit": "TFLOP/s", "ms_per_step": round(wallm / args.steps * 1e3, 4),
+                          "roofline": {"bound": "mfma", "achieved": round(flops / (km_mean * 1e-3) / 1e12, 2),
+                                       "peak": PEAK_TFLOPS["fp8"], "unit": "TFLOP/s",
+                                       "frac": round(flops / (km_mean * 1e-3) / 1e12 / PEAK_TFLOPS["fp8"], 4),
+                                       "traffic": None}}
 
     if args.sparse_density > 0 and args.layout == "bhnd" and d == 128:
         from workloads import random_kv_blocks

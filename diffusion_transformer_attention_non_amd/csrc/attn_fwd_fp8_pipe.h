@@ -311,6 +311,14 @@ void attn_fwd_fp8_pipe_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __r
   i32x8_t kf[2][2];                                     // [key block][d step]
   int ksc = 0;                                          // MX: the K scale word (bytes as qsc's)
   auto read_kfrags = [&](int j) {
+    // MX: the scale words are read first, so that their permute waits for
+    // them alone (LDS reads complete in order), not for the fragments
+    int w0 = 0, w1 = 0;
+    if constexpr (MX) {
+      const char* sb = kslot(j >> 1) + C::kKTile + (j & 1) * 1024 + l32 * 4;
+      w0 = *(const int*)sb;
+      w1 = *(const int*)(sb + 128);
+    }
     const char* kb = kslot(j >> 1) + (j & 1) * 64 * KROW + k_rd;
 #pragma unroll
     for (int b = 0; b < 2; ++b)
@@ -320,10 +328,7 @@ void attn_fwd_fp8_pipe_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __r
         const i32x4_t a1 = *(const i32x4_t*)(kb + b * 32 * KROW + ks * 64 + (MX ? 32 : 16));
         kf[b][ks] = i32x8_t{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
       }
-    if constexpr (MX) {
-      const char* sb = kslot(j >> 1) + C::kKTile + (j & 1) * 1024 + l32 * 4;
-      ksc = __builtin_amdgcn_perm(*(const int*)(sb + 128), *(const int*)sb, sc_sel);
-    }
+    if constexpr (MX) ksc = __builtin_amdgcn_perm(w1, w0, sc_sel);
   };
   // V^T gather (the key order of the P^T packing): lane pair gi>>1 addresses key
   // slot tr_e of an 8-key read; the XOR of the V swizzle depends on key bits
