@@ -103,33 +103,22 @@ __device__ __forceinline__ void dma_b128(i32x4_t rsrc, int voffset, unsigned lds
 
 #define DIT_FENCE() __builtin_amdgcn_sched_barrier(0)
 
-// SPARSE: the key tiles come from a KvBlocks list instead of 0 .. n_t - 1
-// (no key-range split; every workgroup takes one query tile).
-template <class C, bool SPARSE = false>
-__global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void attn_fwd_bf16_pipe_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
-                               const uint16_t* __restrict__ Vg, uint16_t* __restrict__ Og,
-                               float* __restrict__ LSEg, int N, int n_qtiles, float scale_log2, float scale,
-                               PipeSplit split, Layout L, KvBlocks kvb = KvBlocks{nullptr, nullptr, 0}) {
+// One query tile over the key tiles [u0, u1) (dense) or over list positions
+// (SPARSE: the key tiles come from a KvBlocks list instead of 0 .. n_t - 1;
+// a split tile's part `part` of split.parts takes its share of the list).
+// ws_index >= 0: write the rows normalised over this range, with their
+// log2-sum-exp, to workspace slot ws_index; otherwise write O (and the LSE).
+template <class C, bool SPARSE>
+__device__ __forceinline__ void pipe_tile(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
+                                          const uint16_t* __restrict__ Vg, uint16_t* __restrict__ Og,
+                                          float* __restrict__ LSEg, int N, int n_qtiles, float scale_log2,
+                                          const PipeSplit& split, const Layout& L, const KvBlocks& kvb, int tile,
+                                          int u0, int u1, int ws_index, int part) {
   constexpr int D = C::kD, KS = C::kKS, DB = C::kDB;
   constexpr int KROW = C::kKRow, VROW = C::kVRow;
   extern __shared__ __attribute__((aligned(16))) char smem[];
 
   const int n_t = (N + 63) / 64;          // 64-key tiles
-  // query tile and key-tile range [u0, u1) of this workgroup
-  int tile, u0 = 0, u1 = n_t, ws_index = -1, part = 0;
-  if ((int)blockIdx.x < split.n_full) {
-    tile = xcd_remap(blockIdx.x, split.n_full);
-  } else {
-    // neighbouring indices (one XCD) share a key range: K/V reuse in L2
-    const int sidx = xcd_remap(blockIdx.x - split.n_full, gridDim.x - split.n_full);
-    part = sidx / split.n_split;
-    const int ti = sidx - part * split.n_split;
-    tile = split.n_full + ti;
-    u0 = part * n_t / split.parts;
-    u1 = (part + 1) * n_t / split.parts;
-    ws_index = part * split.n_split + ti;
-  }
   const int bh = tile / n_qtiles;
   const int qt = tile - bh * n_qtiles;
   // key tile at pipeline position p: p itself, or the p-th listed one. The
@@ -600,6 +589,115 @@ void attn_fwd_bf16_pipe_kernel(const uint16_t* __restrict__ Qg, const uint16_t* 
         LSEg[(size_t)bh * N + row] = (mc[qb] + __log2f(l_tot)) * 0.6931471805599453f;
     }
   }
+}
+
+template <class C, bool SPARSE = false>
+__global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void attn_fwd_bf16_pipe_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
+                               const uint16_t* __restrict__ Vg, uint16_t* __restrict__ Og,
+                               float* __restrict__ LSEg, int N, int n_qtiles, float scale_log2, float scale,
+                               PipeSplit split, Layout L, KvBlocks kvb = KvBlocks{nullptr, nullptr, 0}) {
+  const int n_t = (N + 63) / 64;
+  // query tile and key-tile range [u0, u1) of this workgroup
+  int tile, u0 = 0, u1 = n_t, ws_index = -1, part = 0;
+  if ((int)blockIdx.x < split.n_full) {
+    tile = xcd_remap(blockIdx.x, split.n_full);
+  } else {
+    // neighbouring indices (one XCD) share a key range: K/V reuse in L2
+    const int sidx = xcd_remap(blockIdx.x - split.n_full, gridDim.x - split.n_full);
+    part = sidx / split.n_split;
+    const int ti = sidx - part * split.n_split;
+    tile = split.n_full + ti;
+    u0 = part * n_t / split.parts;
+    u1 = (part + 1) * n_t / split.parts;
+    ws_index = part * split.n_split + ti;
+  }
+  pipe_tile<C, SPARSE>(Qg, Kg, Vg, Og, LSEg, N, n_qtiles, scale_log2, split, L, kvb, tile, u0, u1, ws_index, part);
+}
+
+// Stream-K schedule: `groups` workgroups (one per CU) cut the tiles * n_t
+// (query tile, key tile) pairs of the call into equal contiguous ranges, so
+// that every CU does the same work whatever the tile count. A range meets at
+// most two tiles partly: the rows of its first tile (if partial) go to
+// workspace slot 2 g, those of its last (if partial, and another tile) to
+// 2 g + 1, and attn_streamk_combine_kernel merges each cut tile; tiles the
+// range covers whole are written directly.
+struct StreamK {
+  float* ws_o;     // [2 groups][256][128]
+  float* ws_lse;   // [2 groups][256], log2 units
+  int groups;
+  int tiles;       // query tiles of the call
+};
+
+template <class C>
+__global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void attn_fwd_bf16_streamk_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
+                                  const uint16_t* __restrict__ Vg, uint16_t* __restrict__ Og,
+                                  float* __restrict__ LSEg, int N, int n_qtiles, float scale_log2, StreamK sk,
+                                  Layout L) {
+  const int n_t = (N + 63) / 64;
+  const long long work = (long long)sk.tiles * n_t;
+  // neighbouring groups (one XCD) share the tile cut between them: K/V reuse in L2
+  const int g = xcd_remap(blockIdx.x, gridDim.x);
+  const long long s = work * g / sk.groups, e = work * (g + 1) / sk.groups;
+  const PipeSplit ws{0, 0, 1, sk.ws_o, sk.ws_lse, nullptr};
+  for (long long pos = s; pos < e;) {
+    const int tile = (int)(pos / n_t);
+    const int u0 = (int)(pos - (long long)tile * n_t);
+    const int u1 = (int)min((long long)n_t, (long long)u0 + (e - pos));
+    const int slot = (u0 == 0 && u1 == n_t) ? -1 : (pos == s ? 2 * g : 2 * g + 1);
+    pipe_tile<C, false>(Qg, Kg, Vg, Og, LSEg, N, n_qtiles, scale_log2, ws, L, KvBlocks{nullptr, nullptr, 0}, tile,
+                        u0, u1, slot, 0);
+    __syncthreads();       // every wave is done with the LDS slots before the next tile's DMA
+    pos += u1 - u0;
+  }
+}
+
+// Merges the tiles cut by stream-K range boundaries. Block (b, row chunk):
+// boundary b (1 .. groups - 1) starts group b; the first boundary inside a
+// tile merges that tile's parts, from the group whose range holds the tile's
+// first key tile to the one holding its last. A group's part is slot 2 g if
+// the part starts the group's range, else 2 g + 1.
+__global__ __launch_bounds__(256) void attn_streamk_combine_kernel(uint16_t* __restrict__ Og, float* __restrict__ LSEg,
+                                                                   int N, int n_qtiles, StreamK sk, Layout L) {
+  constexpr int D = PipeCfg::kD, BR = PipeCfg::kBR;
+  const int b = blockIdx.x / (BR / 8) + 1;
+  const int r = (blockIdx.x % (BR / 8)) * 8 + (threadIdx.x >> 5);
+  const int c = (threadIdx.x & 31) * 4;
+  const int n_t = (N + 63) / 64;
+  const long long work = (long long)sk.tiles * n_t;
+  auto start = [&](int g) { return work * g / sk.groups; };
+  const long long pb = start(b);
+  const int tile = (int)(pb / n_t);
+  const long long t0 = (long long)tile * n_t, t1 = t0 + n_t;
+  if (pb == t0) return;                       // the boundary falls on a tile edge
+  if (start(b - 1) > t0) return;              // an earlier boundary in this tile merges it
+  const int bh = tile / n_qtiles, qt = tile - bh * n_qtiles;
+  const int row = qt * BR + r;
+  if (row >= N) return;
+  int g_hi = b;
+  while (g_hi + 1 < sk.groups && start(g_hi + 1) < t1) ++g_hi;
+  // parts: group b - 1 (its range reaches into the tile from before or starts in it), b .. g_hi
+  auto slot = [&](int g) { return start(g) >= t0 ? 2 * g : 2 * g + 1; };
+  auto empty = [&](int g) { return start(g + 1) == start(g); };   // a group with no work has no part
+  float mx = -INFINITY;
+  for (int g = b - 1; g <= g_hi; ++g)
+    if (!empty(g)) mx = fmaxf(mx, sk.ws_lse[(size_t)slot(g) * BR + r]);
+  float wsum = 0.f;
+  f32x4_t o = {0.f, 0.f, 0.f, 0.f};
+  for (int g = b - 1; g <= g_hi; ++g) {
+    if (empty(g)) continue;
+    const size_t idx = (size_t)slot(g) * BR + r;
+    const float w = fast_exp2(sk.ws_lse[idx] - mx);
+    wsum += w;
+    o += w * *(const f32x4_t*)(sk.ws_o + idx * D + c);
+  }
+  const float inv = 1.0f / wsum;
+  uint2 out;
+  out.x = pack_bf16x2(o[0] * inv, o[1] * inv);
+  out.y = pack_bf16x2(o[2] * inv, o[3] * inv);
+  *(uint2*)(Og + L.out_off(bh) + (long long)row * L.on + c) = out;
+  if (LSEg != nullptr && c == 0) LSEg[(size_t)bh * N + row] = (mx + __log2f(wsum)) * 0.6931471805599453f;
 }
 
 #undef DIT_FENCE

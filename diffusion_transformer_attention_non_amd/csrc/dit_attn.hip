@@ -42,7 +42,10 @@ hipError_t allow_lds_pipe() {
   const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_fwd_bf16_pipe_kernel<C, false>),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, C::kLdsBytes);
   if (e != hipSuccess) return e;
-  return hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_fwd_bf16_pipe_kernel<C, true>),
+  const hipError_t e2 = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_fwd_bf16_pipe_kernel<C, true>),
+                                            hipFuncAttributeMaxDynamicSharedMemorySize, C::kLdsBytes);
+  if (e2 != hipSuccess) return e2;
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_fwd_bf16_streamk_kernel<C>),
                              hipFuncAttributeMaxDynamicSharedMemorySize, C::kLdsBytes);
 }
 template <class C>
@@ -173,6 +176,50 @@ int plan_split(int BH, int n_qtiles, int N, int key_tile, int n_cu, PipeSplit* s
   return 1;
 }
 
+// Cost of a schedule in key tiles on the busiest CU, each tile a workgroup
+// touches adding kPartOverhead (prologue, epilogue). The split plan: its full
+// rounds, then the last round's parts. Stream-K: the equal share, touching
+// share / n_t + 1 tiles.
+double split_cost(const PipeSplit& sp, int tiles, int n_t, int n_cu) {
+  if (sp.n_split == 0) return (double)((tiles + n_cu - 1) / n_cu) * (n_t + kPartOverhead);
+  const long long waves = ((long long)sp.n_split * sp.parts + n_cu - 1) / n_cu;
+  return (double)(sp.n_full / n_cu) * (n_t + kPartOverhead) + (double)waves * ((double)n_t / sp.parts + kPartOverhead);
+}
+double streamk_cost(int tiles, int n_t, int groups) {
+  const double share = (double)tiles * n_t / groups;
+  return share + kPartOverhead * (share / n_t + 1.0);
+}
+constexpr int kStreamKMinKeyTiles = 4;        // per group
+
+// Dense bf16 d = 128 under stream-K: `groups` workgroups, partial rows in a
+// stream-ordered workspace of 2 groups slots, merged by the combine kernel.
+// Returns 1 if it launched (status in *status), 0 if the workspace could not
+// be had (the caller then runs the split plan).
+template <class C>
+int launch_streamk(const void* q, const void* k, const void* v, void* o, float* lse, int tiles, int N,
+                   int n_qtiles, float scale_log2, hipStream_t st, int groups, const Layout& L, int* status) {
+  const size_t units = (size_t)2 * groups * C::kBR;
+  void* ws = nullptr;
+  if (hipMallocAsync(&ws, units * (C::kD + 1) * sizeof(float), st) != hipSuccess || ws == nullptr) {
+    (void)hipGetLastError();
+    return 0;
+  }
+  StreamK sk{static_cast<float*>(ws), static_cast<float*>(ws) + units * C::kD, groups, tiles};
+  hipLaunchKernelGGL(attn_fwd_bf16_streamk_kernel<C>, dim3((unsigned)groups), dim3(C::kThreads), C::kLdsBytes, st,
+                     static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                     static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), lse, N, n_qtiles, scale_log2, sk,
+                     L);
+  hipError_t err = hipGetLastError();
+  if (err == hipSuccess && groups > 1) {
+    hipLaunchKernelGGL(attn_streamk_combine_kernel, dim3((unsigned)((groups - 1) * (C::kBR / 8))), dim3(256), 0, st,
+                       static_cast<uint16_t*>(o), lse, N, n_qtiles, sk, L);
+    err = hipGetLastError();
+  }
+  (void)hipFreeAsync(ws, st);
+  *status = err == hipSuccess ? DIT_ATTN_OK : DIT_ATTN_ELAUNCH;
+  return 1;
+}
+
 // SPARSE: block lists in kvb; the split planner then takes max_blocks as
 // the key-tile count (the host never reads the lists).
 template <class C, bool SPARSE = false>
@@ -184,6 +231,23 @@ int launch_pipe(const void* q, const void* k, const void* v, void* o, float* lse
   const float scale_log2 = scale * 1.4426950408889634f;
   PipeSplit sp;
   void* ws = nullptr;
+  if (!SPARSE) {
+    const int n_t = (N + 63) / 64;
+    const long long per_group = (long long)tiles * n_t / kStreamKMinKeyTiles;
+    const int groups = (int)std::min<long long>(n_cu, per_group);
+    PipeSplit plan;
+    plan_split((int)tiles, 1, N, 64, n_cu, &plan);
+    // Stream-K only up to two rounds of tiles: a CU's range then stays in
+    // one or two heads. With more rounds the ranges run through every head at
+    // once and K/V stop fitting the caches (measured 7-8% slower at H = 12
+    // and 24 of the 16896-token call, where the split plan does well).
+    if (groups >= 2 && tiles <= 2LL * n_cu &&
+        streamk_cost((int)tiles, n_t, groups) < split_cost(plan, (int)tiles, n_t, n_cu)) {
+      int status = DIT_ATTN_OK;
+      if (launch_streamk<C>(q, k, v, o, lse, (int)tiles, N, n_qtiles, scale_log2, st, groups, L, &status))
+        return status;
+    }
+  }
   const int keys_planned = SPARSE ? kvb.max_blocks * 64 : N;
   if (plan_split(BH, n_qtiles, keys_planned, 64, n_cu, &sp)) {
     const size_t units = (size_t)sp.n_split * sp.parts * C::kBR;

@@ -20,13 +20,15 @@
  *            innermost, in device memory. o is always bfloat16.
  * Ownership: the caller allocates, owns and frees every buffer it passes.
  *            One internal buffer exists: when a bf16 d = 128 call would leave
- *            the GPU's last round of workgroups partly filled, those query
- *            tiles are split along the keys and their fp32 partial rows go to
- *            a stream-ordered scratch buffer (hipMallocAsync on `stream`,
+ *            the GPU's last round of workgroups partly filled, query tiles are
+ *            split along the keys (the last round's tiles, or, for calls of at
+ *            most two rounds, every CU taking an equal share of all (query
+ *            tile, key tile) pairs) and their fp32 partial rows go to a
+ *            stream-ordered scratch buffer (hipMallocAsync on `stream`,
  *            released by hipFreeAsync on `stream` after the merge; at most
- *            CUs x 256 rows x 129 floats, 33.8 MB on a 256-CU MI355X). If that
- *            allocation fails the call runs unsplit, with the same result
- *            semantics. The library retains no memory, never synchronises,
+ *            2 x CUs x 256 rows x 129 floats, 67.6 MB on a 256-CU MI355X). If
+ *            that allocation fails the call runs without it, with the same
+ *            result semantics. The library retains no memory, never synchronises,
  *            and keeps no state beyond its loaded code objects and a
  *            per-device record (gfx950 or not, CU count).
  * Streams:   work is enqueued on `stream` (a hipStream_t; NULL = the null
