@@ -24,8 +24,19 @@ DIT_ATTN_SPARSE_KV_BLOCK = 64
 DIT_ATTN_MX_ALONG_D = 0
 DIT_ATTN_MX_ALONG_TOKENS = 1
 
+DIT_ATTN_SCHED_TILE = 0
+DIT_ATTN_SCHED_SPLIT = 1
+DIT_ATTN_SCHED_STREAMK = 2
+
 EXPORTED = ("dit_attn_fwd", "dit_attn_fwd_blocksparse", "dit_attn_fwd_ex", "dit_attn_fwd_mx", "dit_attn_fwd_strided",
-            "dit_attn_quantize_e4m3", "dit_attn_quantize_mx", "dit_attn_strerror", "dit_attn_version")
+            "dit_attn_plan", "dit_attn_quantize_e4m3", "dit_attn_quantize_mx", "dit_attn_strerror",
+            "dit_attn_version")
+
+
+class DitAttnPlan(ctypes.Structure):
+    """dit_attn_plan_t."""
+    _fields_ = [("schedule", ctypes.c_int32), ("workgroups", ctypes.c_int32), ("parts", ctypes.c_int32),
+                ("split_tiles", ctypes.c_int32), ("workspace_bytes", ctypes.c_int64)]
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is not built; run `python -m diffusion_transformer_attention_non_amd.build` "
@@ -46,6 +57,8 @@ _lib.dit_attn_fwd_mx.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, 
 _lib.dit_attn_fwd_mx.restype = _i
 _lib.dit_attn_quantize_mx.argtypes = [_vp, _i, _i, _i, _i, _i, _vp, _vp, _vp]
 _lib.dit_attn_quantize_mx.restype = _i
+_lib.dit_attn_plan.argtypes = [_i, _i, _i, _i, _i, _i, _i, _i, ctypes.POINTER(DitAttnPlan)]
+_lib.dit_attn_plan.restype = _i
 _lib.dit_attn_quantize_e4m3.argtypes = [_vp, _i64, _vp, _vp, _vp, _vp]
 _lib.dit_attn_quantize_e4m3.restype = _i
 _lib.dit_attn_strerror.argtypes = [_i]
@@ -104,6 +117,13 @@ def dit_attn_fwd_mx(q8, k8, v8, q_scales, k_scales, v_scales, o, B, H, N, d, sca
 
 def dit_attn_quantize_mx(x, B, H, N, d, along, x8, scales, stream=None) -> int:
     return _lib.dit_attn_quantize_mx(_ptr(x), B, H, N, d, along, _ptr(x8), _ptr(scales), _ptr(stream))
+
+
+def dit_attn_plan(B, H, N, d, dtype, max_blocks=0, lse=False, n_cu=0):
+    """Returns (status, DitAttnPlan)."""
+    plan = DitAttnPlan()
+    st = _lib.dit_attn_plan(B, H, N, d, dtype, max_blocks, 1 if lse else 0, n_cu, ctypes.byref(plan))
+    return st, plan
 
 
 def dit_attn_quantize_e4m3(x, n, x8, descale, amax_ws, stream=None) -> int:

@@ -191,6 +191,58 @@ double streamk_cost(int tiles, int n_t, int groups) {
 }
 constexpr int kStreamKMinKeyTiles = 4;        // per group
 
+// The schedule of one call, decided on the host from its shape alone (never
+// from the data). Both the launch and dit_attn_plan use this.
+enum PlanKind { kPlanBf16D128 = 0, kPlanBf16D128Sparse = 1, kPlanFp8D128 = 2, kPlanBf16D64 = 3 };
+struct Plan {
+  int schedule;          // DIT_ATTN_SCHED_*
+  PipeSplit sp;          // split: n_full, n_split, parts (workspace pointers unset)
+  int groups;            // stream-K workgroups
+  long long workgroups;  // of the attention kernel
+  size_t units;          // partial rows in the workspace
+  size_t ws_floats;      // workspace size in floats
+};
+
+int make_plan(int kind, long long BH, int N, int n_cu, int max_blocks, bool lse, Plan* p) {
+  const int br = kind == kPlanBf16D64 ? CfgBf16D64::kBR : CfgBf16D128::kBR;
+  const long long n_qtiles = (N + br - 1) / br;
+  const long long tiles = n_qtiles * BH;
+  if (tiles > 0x7fffffffLL / 8) return DIT_ATTN_EINVAL;
+  *p = Plan{DIT_ATTN_SCHED_TILE, PipeSplit{(int)tiles, 0, 1, nullptr, nullptr, nullptr}, 0, tiles, 0, 0};
+  if (kind == kPlanBf16D64) return DIT_ATTN_OK;
+  constexpr int kD = CfgBf16D128::kD, kBR = CfgBf16D128::kBR;
+  if (kind == kPlanBf16D128) {
+    const int n_t = (N + 63) / 64;
+    const int groups = (int)std::min<long long>(n_cu, tiles * n_t / kStreamKMinKeyTiles);
+    PipeSplit alt;
+    plan_split((int)tiles, 1, N, 64, n_cu, &alt);
+    // Stream-K only up to two rounds of tiles: a CU's range then stays in
+    // one or two heads. With more rounds the ranges run through every head at
+    // once and K/V stop fitting the caches (measured 7-8% slower at H = 12
+    // and 24 of the 16896-token call, where the split plan does well).
+    if (groups >= 2 && tiles <= 2LL * n_cu &&
+        streamk_cost((int)tiles, n_t, groups) < split_cost(alt, (int)tiles, n_t, n_cu)) {
+      p->schedule = DIT_ATTN_SCHED_STREAMK;
+      p->groups = groups;
+      p->workgroups = groups;
+      p->units = (size_t)2 * groups * kBR;
+      p->ws_floats = p->units * (kD + 1);
+      return DIT_ATTN_OK;
+    }
+  }
+  const int keys = kind == kPlanBf16D128Sparse ? max_blocks * 64 : N;
+  const int key_tile = kind == kPlanFp8D128 ? CfgFp8D128::kKB : 64;
+  if (plan_split((int)BH, (int)n_qtiles, keys, key_tile, n_cu, &p->sp)) {
+    p->schedule = DIT_ATTN_SCHED_SPLIT;
+    p->workgroups = (long long)p->sp.n_full + (long long)p->sp.n_split * p->sp.parts;
+    p->units = (size_t)p->sp.n_split * p->sp.parts * kBR;
+    // fp8 with an LSE output: O's merge weights come from the e4m3 sums, the
+    // LSE from exact sums of its own
+    p->ws_floats = p->units * (kD + 1) + (kind == kPlanFp8D128 && lse ? p->units : 0);
+  }
+  return DIT_ATTN_OK;
+}
+
 // Dense bf16 d = 128 under stream-K: `groups` workgroups, partial rows in a
 // stream-ordered workspace of 2 groups slots, merged by the combine kernel.
 // Returns 1 if it launched (status in *status), 0 if the workspace could not
@@ -225,39 +277,29 @@ int launch_streamk(const void* q, const void* k, const void* v, void* o, float* 
 template <class C, bool SPARSE = false>
 int launch_pipe(const void* q, const void* k, const void* v, void* o, float* lse, int BH, int N,
                 float scale, hipStream_t st, int n_cu, const Layout& L, const KvBlocks& kvb = KvBlocks{}) {
+  Plan plan;
+  const int pst = make_plan(SPARSE ? kPlanBf16D128Sparse : kPlanBf16D128, BH, N, n_cu, kvb.max_blocks, lse != nullptr,
+                            &plan);
+  if (pst != DIT_ATTN_OK) return pst;
   const int n_qtiles = (N + C::kBR - 1) / C::kBR;
-  const long long tiles = (long long)n_qtiles * BH;
-  if (tiles > 0x7fffffffLL / 8) return DIT_ATTN_EINVAL;
+  const int tiles = n_qtiles * BH;
   const float scale_log2 = scale * 1.4426950408889634f;
-  PipeSplit sp;
-  void* ws = nullptr;
-  if (!SPARSE) {
-    const int n_t = (N + 63) / 64;
-    const long long per_group = (long long)tiles * n_t / kStreamKMinKeyTiles;
-    const int groups = (int)std::min<long long>(n_cu, per_group);
-    PipeSplit plan;
-    plan_split((int)tiles, 1, N, 64, n_cu, &plan);
-    // Stream-K only up to two rounds of tiles: a CU's range then stays in
-    // one or two heads. With more rounds the ranges run through every head at
-    // once and K/V stop fitting the caches (measured 7-8% slower at H = 12
-    // and 24 of the 16896-token call, where the split plan does well).
-    if (groups >= 2 && tiles <= 2LL * n_cu &&
-        streamk_cost((int)tiles, n_t, groups) < split_cost(plan, (int)tiles, n_t, n_cu)) {
-      int status = DIT_ATTN_OK;
-      if (launch_streamk<C>(q, k, v, o, lse, (int)tiles, N, n_qtiles, scale_log2, st, groups, L, &status))
-        return status;
-    }
+  if (plan.schedule == DIT_ATTN_SCHED_STREAMK) {
+    int status = DIT_ATTN_OK;
+    if (launch_streamk<C>(q, k, v, o, lse, tiles, N, n_qtiles, scale_log2, st, plan.groups, L, &status)) return status;
+    // no workspace: the split plan without its workspace is one workgroup per tile
+    plan.schedule = DIT_ATTN_SCHED_TILE;
   }
-  const int keys_planned = SPARSE ? kvb.max_blocks * 64 : N;
-  if (plan_split(BH, n_qtiles, keys_planned, 64, n_cu, &sp)) {
-    const size_t units = (size_t)sp.n_split * sp.parts * C::kBR;
-    if (hipMallocAsync(&ws, units * (C::kD + 1) * sizeof(float), st) == hipSuccess && ws != nullptr) {
+  PipeSplit sp = PipeSplit{tiles, 0, 1, nullptr, nullptr, nullptr};
+  void* ws = nullptr;
+  if (plan.schedule == DIT_ATTN_SCHED_SPLIT) {
+    if (hipMallocAsync(&ws, plan.ws_floats * sizeof(float), st) == hipSuccess && ws != nullptr) {
+      sp = plan.sp;
       sp.ws_o = static_cast<float*>(ws);
-      sp.ws_lse = sp.ws_o + units * C::kD;
+      sp.ws_lse = sp.ws_o + plan.units * C::kD;
     } else {
       (void)hipGetLastError();
       ws = nullptr;
-      sp = PipeSplit{(int)tiles, 0, 1, nullptr, nullptr};
     }
   }
   const long long grid = (long long)sp.n_full + (long long)sp.n_split * sp.parts;
@@ -283,25 +325,24 @@ template <class C, bool MX = false>
 int launch_fp8(const void* q, const void* k, const void* v, void* o, float* lse, const float* descale,
                int BH, int N, float scale, hipStream_t st, int n_cu, const Layout& L,
                const MxScales& mxs = MxScales{nullptr, nullptr, nullptr}) {
-  const int n_qtiles = (N + C::kBR - 1) / C::kBR;
-  const long long tiles = (long long)n_qtiles * BH;
-  if (tiles > 0x7fffffffLL / 8) return DIT_ATTN_EINVAL;
   static_assert(C::kBR == PipeCfg::kBR && C::kD == PipeCfg::kD, "the merge kernel assumes 256 x 128 tiles");
+  Plan plan;
+  const int pst = make_plan(kPlanFp8D128, BH, N, n_cu, 0, lse != nullptr, &plan);
+  if (pst != DIT_ATTN_OK) return pst;
+  const int n_qtiles = (N + C::kBR - 1) / C::kBR;
+  const int tiles = n_qtiles * BH;
   const float scale_log2 = scale * 1.4426950408889634f;
-  PipeSplit sp;
+  PipeSplit sp = PipeSplit{tiles, 0, 1, nullptr, nullptr, nullptr};
   void* ws = nullptr;
-  if (plan_split(BH, n_qtiles, N, C::kKB, n_cu, &sp)) {
-    const size_t units = (size_t)sp.n_split * sp.parts * C::kBR;
-    // O's merge weights come from the e4m3 sums; an LSE output has exact sums of its own
-    const size_t floats = units * (C::kD + 1) + (lse != nullptr ? units : 0);
-    if (hipMallocAsync(&ws, floats * sizeof(float), st) == hipSuccess && ws != nullptr) {
+  if (plan.schedule == DIT_ATTN_SCHED_SPLIT) {
+    if (hipMallocAsync(&ws, plan.ws_floats * sizeof(float), st) == hipSuccess && ws != nullptr) {
+      sp = plan.sp;
       sp.ws_o = static_cast<float*>(ws);
-      sp.ws_lse = sp.ws_o + units * C::kD;
-      sp.ws_lse_out = lse != nullptr ? sp.ws_lse + units : nullptr;
+      sp.ws_lse = sp.ws_o + plan.units * C::kD;
+      sp.ws_lse_out = lse != nullptr ? sp.ws_lse + plan.units : nullptr;
     } else {
       (void)hipGetLastError();
       ws = nullptr;
-      sp = PipeSplit{(int)tiles, 0, 1, nullptr, nullptr};
     }
   }
   const long long grid = (long long)sp.n_full + (long long)sp.n_split * sp.parts;
@@ -374,7 +415,7 @@ int check_call(const void* q, const void* k, const void* v, void* o, int B, int 
 
 extern "C" {
 
-int dit_attn_version(void) { return (1 << 16) | 3; }
+int dit_attn_version(void) { return (1 << 16) | 4; }
 
 const char* dit_attn_strerror(int status) {
   switch (status) {
@@ -430,6 +471,35 @@ int dit_attn_fwd_blocksparse(const void* q, const void* k, const void* v, void* 
   const KvBlocks kvb{kv_blocks, kv_counts, max_blocks};
   return launch_pipe<C, true>(q, k, v, o, lse, c.bh, N, scale, static_cast<hipStream_t>(stream), cu_count(), c.L,
                               kvb);
+}
+
+int dit_attn_plan(int B, int H, int N, int d, int dtype, int max_blocks, int lse, int n_cu, dit_attn_plan_t* plan) {
+  if (!plan || B < 1 || H < 1 || N < 1 || n_cu < 0 || max_blocks < 0) return DIT_ATTN_EINVAL;
+  if (dtype != DIT_ATTN_BF16 && dtype != DIT_ATTN_FP8_E4M3) return DIT_ATTN_EUNSUPPORTED;
+  if (dtype == DIT_ATTN_BF16 && d != 64 && d != 128) return DIT_ATTN_EUNSUPPORTED;
+  if (dtype == DIT_ATTN_FP8_E4M3 && d != 128) return DIT_ATTN_EUNSUPPORTED;
+  if (max_blocks > 0 && (dtype != DIT_ATTN_BF16 || d != 128)) return DIT_ATTN_EUNSUPPORTED;
+  if (max_blocks > (N + 63) / 64) return DIT_ATTN_EINVAL;
+  const long long bh = (long long)B * H;
+  if (bh > 0x7fffffffLL) return DIT_ATTN_EINVAL;
+  if (n_cu == 0) {
+    const int dev_status = check_device();
+    if (dev_status != DIT_ATTN_OK) return dev_status;
+    n_cu = cu_count();
+  }
+  const int kind = dtype == DIT_ATTN_FP8_E4M3 ? kPlanFp8D128
+                   : d == 64                  ? kPlanBf16D64
+                   : max_blocks > 0           ? kPlanBf16D128Sparse
+                                              : kPlanBf16D128;
+  Plan p;
+  const int st = make_plan(kind, bh, N, n_cu, max_blocks, lse != 0, &p);
+  if (st != DIT_ATTN_OK) return st;
+  plan->schedule = p.schedule;
+  plan->workgroups = (int32_t)p.workgroups;
+  plan->parts = p.schedule == DIT_ATTN_SCHED_SPLIT ? p.sp.parts : 1;
+  plan->split_tiles = p.schedule == DIT_ATTN_SCHED_SPLIT ? p.sp.n_split : 0;
+  plan->workspace_bytes = (int64_t)(p.ws_floats * sizeof(float));
+  return DIT_ATTN_OK;
 }
 
 int dit_attn_fwd_ex(const void* q, const void* k, const void* v, void* o, int B, int H, int N, int d,

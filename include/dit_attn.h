@@ -250,11 +250,42 @@ DIT_ATTN_API int dit_attn_quantize_mx(const void* x, int B, int H, int N, int d,
 DIT_ATTN_API int dit_attn_quantize_e4m3(const void* x, int64_t n, void* x8, float* descale,
                            uint32_t* amax_ws, void* stream);
 
+/* Schedules of an attention call (dit_attn_plan_t.schedule). */
+#define DIT_ATTN_SCHED_TILE 0     /* one workgroup per query tile */
+#define DIT_ATTN_SCHED_SPLIT 1    /* the last round's query tiles split along the keys, then merged */
+#define DIT_ATTN_SCHED_STREAMK 2  /* every CU takes an equal share of (query tile, key tile) pairs */
+
+typedef struct {
+    int32_t schedule;         /* DIT_ATTN_SCHED_* */
+    int32_t workgroups;       /* workgroups of the attention kernel */
+    int32_t parts;            /* key ranges per split query tile (SPLIT), else 1 */
+    int32_t split_tiles;      /* query tiles split along the keys (SPLIT), else 0 */
+    int64_t workspace_bytes;  /* stream-ordered scratch the call allocates and frees, 0 if none */
+} dit_attn_plan_t;
+
+/*
+ * dit_attn_plan - the schedule an attention call of this shape would use.
+ *
+ * The launch decides its schedule from the shape alone (never from the
+ * data); this returns that decision without launching anything, so a caller
+ * can size memory or check the plan. B, H, N, d, dtype as for dit_attn_fwd;
+ * max_blocks > 0 describes a dit_attn_fwd_blocksparse call with that list
+ * length (bf16, d = 128 only), 0 a dense call (the block-scaled fp8 call
+ * plans as DIT_ATTN_FP8_E4M3); lse != 0 if an LSE output is requested.
+ * n_cu: compute units to plan for; 0 means the current device's (then a
+ * gfx950 device must be current, else DIT_ATTN_EDEVICE).
+ * plan   : host pointer, filled on DIT_ATTN_OK.
+ * Status: DIT_ATTN_EINVAL (NULL plan, sizes < 1, n_cu < 0, max_blocks out
+ * of range), DIT_ATTN_EUNSUPPORTED (d, dtype), DIT_ATTN_EDEVICE.
+ */
+DIT_ATTN_API int dit_attn_plan(int B, int H, int N, int d, int dtype, int max_blocks, int lse, int n_cu,
+                  dit_attn_plan_t* plan);
+
 /* Human-readable name of a status code (static string, never NULL). */
 DIT_ATTN_API const char* dit_attn_strerror(int status);
 
 /* Library ABI version: (major << 16) | minor (1.1 adds dit_attn_fwd_strided,
-   1.2 dit_attn_fwd_blocksparse, 1.3 dit_attn_fwd_mx and dit_attn_quantize_mx). */
+   1.2 dit_attn_fwd_blocksparse, 1.3 dit_attn_fwd_mx and dit_attn_quantize_mx, 1.4 dit_attn_plan). */
 DIT_ATTN_API int dit_attn_version(void);
 
 #ifdef __cplusplus

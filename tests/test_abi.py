@@ -24,8 +24,8 @@ def lib():
 
 def test_header_declares_the_entry_points():
     assert _declared() == sorted(["dit_attn_fwd", "dit_attn_fwd_blocksparse", "dit_attn_fwd_ex", "dit_attn_fwd_mx",
-                                  "dit_attn_fwd_strided", "dit_attn_quantize_e4m3", "dit_attn_quantize_mx",
-                                  "dit_attn_strerror", "dit_attn_version"])
+                                  "dit_attn_fwd_strided", "dit_attn_plan", "dit_attn_quantize_e4m3",
+                                  "dit_attn_quantize_mx", "dit_attn_strerror", "dit_attn_version"])
 
 
 def test_library_exports_every_declared_symbol(lib):

@@ -67,3 +67,14 @@ def test_streamk_strided_rows_bitwise_and_deterministic():
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
     assert torch.equal(o3, o1) and torch.equal(l3, l1)
     assert not torch.isnan(out).any()
+
+
+def test_plan_for_the_current_device():
+    import diffusion_transformer_attention_non_amd as dit
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    st, p = dit.dit_attn_plan(1, 3, 16896, 128, dit.DIT_ATTN_BF16, 0, 0, 0)
+    assert st == dit.DIT_ATTN_OK
+    st2, p2 = dit.dit_attn_plan(1, 3, 16896, 128, dit.DIT_ATTN_BF16, 0, 0, n_cu)
+    assert st2 == dit.DIT_ATTN_OK
+    assert (p.schedule, p.workgroups, p.workspace_bytes) == (p2.schedule, p2.workgroups, p2.workspace_bytes)
+    say(f"[gpu] plan H=3 N=16896 on {n_cu} CUs: schedule {p.schedule}, {p.workgroups} workgroups")

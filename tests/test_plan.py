@@ -1,0 +1,111 @@
+"""Host logic of the launch schedule, through dit_attn_plan (no GPU: an
+explicit CU count). The launch itself calls the same planner, so these pin
+what the kernels are given: one workgroup per 256-row query tile, the last
+round's tiles split along the keys when that shortens the last round, or
+stream-K for calls of at most two rounds when it is cheaper."""
+import itertools
+
+import pytest
+
+import diffusion_transformer_attention_non_amd as dit
+
+BF16, FP8 = dit.DIT_ATTN_BF16, dit.DIT_ATTN_FP8_E4M3
+TILE, SPLIT, STREAMK = dit.DIT_ATTN_SCHED_TILE, dit.DIT_ATTN_SCHED_SPLIT, dit.DIT_ATTN_SCHED_STREAMK
+ROW_BYTES = 129 * 4        # a partial row: 128 fp32 values and its log-sum-exp
+
+
+def plan(B, H, N, d=128, dtype=BF16, max_blocks=0, lse=False, n_cu=256):
+    st, p = dit.dit_attn_plan(B, H, N, d, dtype, max_blocks, lse, n_cu)
+    assert st == dit.DIT_ATTN_OK, st
+    return p
+
+
+def test_headline_shape_splits_its_last_round():
+    # 24 heads x 66 tiles = 1584 = 6 rounds of 256 + 48: those 48 split into 5 key ranges
+    p = plan(1, 24, 16896)
+    assert (p.schedule, p.parts, p.split_tiles) == (SPLIT, 5, 48)
+    assert p.workgroups == 1584 - 48 + 48 * 5
+    assert p.workspace_bytes == 48 * 5 * 256 * ROW_BYTES
+
+
+@pytest.mark.parametrize("H", [1, 3, 5, 6])
+def test_per_gpu_shares_use_streamk(H):
+    """At most two rounds of tiles (H <= 7 at 66 tiles a head): every CU takes an
+    equal share; two workspace slots of 256 partial rows per CU. (H = 4, 264
+    tiles, is the near tie where splitting the 8 tiles past one round costs
+    the same.)"""
+    p = plan(1, H, 16896)
+    assert p.schedule == STREAMK and p.workgroups == 256 and p.parts == 1 and p.split_tiles == 0
+    assert p.workspace_bytes == 2 * 256 * 256 * ROW_BYTES
+
+
+def test_many_rounds_never_streamk():
+    for H in range(8, 49):
+        p = plan(1, H, 16896)
+        assert p.schedule in (TILE, SPLIT), H
+
+
+def test_tiny_and_d64_calls_run_one_workgroup_per_tile():
+    p = plan(1, 1, 256)
+    assert (p.schedule, p.workgroups, p.workspace_bytes) == (TILE, 1, 0)
+    p = plan(1, 2, 256, d=64)
+    assert p.schedule == TILE and p.workspace_bytes == 0
+
+
+def test_fp8_plans_over_128_key_tiles_and_lse_adds_exact_sums():
+    p = plan(1, 24, 16896, dtype=FP8)
+    q = plan(1, 24, 16896, dtype=FP8, lse=True)
+    assert p.schedule == SPLIT and p.split_tiles == 48
+    units = p.split_tiles * p.parts * 256
+    assert p.workspace_bytes == units * ROW_BYTES
+    assert q.workspace_bytes == units * ROW_BYTES + units * 4
+    # the fp8 path never takes stream-K
+    assert plan(1, 3, 16896, dtype=FP8).schedule != STREAMK
+
+
+def test_blocksparse_plans_with_the_list_length():
+    full = plan(1, 24, 16896)
+    short = plan(1, 24, 16896, max_blocks=20)       # 20 key tiles: at most 5 parts of 4
+    assert short.schedule in (TILE, SPLIT) and short.parts <= 5
+    assert plan(1, 3, 16896, max_blocks=264).schedule != STREAMK
+    assert full.parts >= short.parts
+
+
+@pytest.mark.parametrize("n_cu", [80, 104, 228, 256, 304])
+def test_plan_invariants_over_shapes(n_cu):
+    for B, H, N in itertools.product([1, 2], [1, 2, 3, 6, 12, 24], [64, 300, 4608, 16896, 25088]):
+        tiles = B * H * -(-N // 256)
+        n_t = -(-N // 64)
+        p = plan(B, H, N, n_cu=n_cu)
+        if p.schedule == TILE:
+            assert p.workgroups == tiles and p.workspace_bytes == 0
+        elif p.schedule == SPLIT:
+            assert p.split_tiles == tiles % n_cu and p.parts >= 2
+            assert n_t // p.parts >= 4                                   # at least 4 key tiles a range
+            assert p.workgroups == tiles - p.split_tiles + p.split_tiles * p.parts
+            assert p.workspace_bytes == p.split_tiles * p.parts * 256 * ROW_BYTES
+            # a split last round must not take more waves than it saves
+            assert -(-p.split_tiles * p.parts // n_cu) < p.parts
+        else:
+            assert tiles <= 2 * n_cu
+            assert p.workgroups == min(n_cu, tiles * n_t // 4) and p.workgroups >= 2
+            assert p.workspace_bytes == 2 * p.workgroups * 256 * ROW_BYTES
+
+
+def test_plan_rejects_bad_arguments():
+    bad = [((0, 1, 64, 128, BF16, 0, 0, 256), dit.DIT_ATTN_EINVAL),
+           ((1, 1, 64, 96, BF16, 0, 0, 256), dit.DIT_ATTN_EUNSUPPORTED),
+           ((1, 1, 64, 64, FP8, 0, 0, 256), dit.DIT_ATTN_EUNSUPPORTED),
+           ((1, 1, 64, 128, 7, 0, 0, 256), dit.DIT_ATTN_EUNSUPPORTED),
+           ((1, 1, 64, 128, BF16, 2, 0, 256), dit.DIT_ATTN_EINVAL),          # max_blocks past ceil(N/64)
+           ((1, 1, 64, 64, BF16, 1, 0, 256), dit.DIT_ATTN_EUNSUPPORTED),     # sparse needs d = 128
+           ((1, 1, 64, 128, BF16, 0, 0, -1), dit.DIT_ATTN_EINVAL)]
+    for args, want in bad:
+        assert dit.dit_attn_plan(*args)[0] == want, args
+
+
+def test_plan_for_the_current_device_needs_one():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert dit.dit_attn_plan(1, 1, 64, 128, BF16, 0, 0, 0)[0] == dit.DIT_ATTN_EDEVICE
