@@ -653,17 +653,21 @@ void attn_fwd_bf16_streamk_kernel(const uint16_t* __restrict__ Qg, const uint16_
   }
 }
 
-// Merges the tiles cut by stream-K range boundaries. Block (b, row chunk):
+// Merges the tiles cut by stream-K range boundaries. Block (b, 64-row chunk):
 // boundary b (1 .. groups - 1) starts group b; the first boundary inside a
 // tile merges that tile's parts, from the group whose range holds the tile's
 // first key tile to the one holding its last. A group's part is slot 2 g if
-// the part starts the group's range, else 2 g + 1.
+// the part starts the group's range, else 2 g + 1. The boundary arithmetic
+// is done once per block; each thread then takes 4 values of 8 rows, four
+// rows' loads in flight at a time.
+constexpr int kStreamKMergeRows = 64;
+constexpr int kStreamKMaxParts = 16;          // parts of one cut tile; the planner keeps ranges long enough
 __global__ __launch_bounds__(256) void attn_streamk_combine_kernel(uint16_t* __restrict__ Og, float* __restrict__ LSEg,
                                                                    int N, int n_qtiles, StreamK sk, Layout L) {
-  constexpr int D = PipeCfg::kD, BR = PipeCfg::kBR;
-  const int b = blockIdx.x / (BR / 8) + 1;
-  const int r = (blockIdx.x % (BR / 8)) * 8 + (threadIdx.x >> 5);
-  const int c = (threadIdx.x & 31) * 4;
+  constexpr int D = PipeCfg::kD, BR = PipeCfg::kBR, CHUNKS = BR / kStreamKMergeRows;
+  constexpr int kMaxParts = kStreamKMaxParts;
+  const int b = blockIdx.x / CHUNKS + 1;
+  const int chunk = blockIdx.x % CHUNKS;
   const int n_t = (N + 63) / 64;
   const long long work = (long long)sk.tiles * n_t;
   auto start = [&](int g) { return work * g / sk.groups; };
@@ -672,32 +676,40 @@ __global__ __launch_bounds__(256) void attn_streamk_combine_kernel(uint16_t* __r
   const long long t0 = (long long)tile * n_t, t1 = t0 + n_t;
   if (pb == t0) return;                       // the boundary falls on a tile edge
   if (start(b - 1) > t0) return;              // an earlier boundary in this tile merges it
-  const int bh = tile / n_qtiles, qt = tile - bh * n_qtiles;
-  const int row = qt * BR + r;
-  if (row >= N) return;
-  int g_hi = b;
-  while (g_hi + 1 < sk.groups && start(g_hi + 1) < t1) ++g_hi;
-  // parts: group b - 1 (its range reaches into the tile from before or starts in it), b .. g_hi
-  auto slot = [&](int g) { return start(g) >= t0 ? 2 * g : 2 * g + 1; };
-  auto empty = [&](int g) { return start(g + 1) == start(g); };   // a group with no work has no part
-  float mx = -INFINITY;
-  for (int g = b - 1; g <= g_hi; ++g)
-    if (!empty(g)) mx = fmaxf(mx, sk.ws_lse[(size_t)slot(g) * BR + r]);
-  float wsum = 0.f;
-  f32x4_t o = {0.f, 0.f, 0.f, 0.f};
-  for (int g = b - 1; g <= g_hi; ++g) {
-    if (empty(g)) continue;
-    const size_t idx = (size_t)slot(g) * BR + r;
-    const float w = fast_exp2(sk.ws_lse[idx] - mx);
-    wsum += w;
-    o += w * *(const f32x4_t*)(sk.ws_o + idx * D + c);
+  // the parts: group b - 1 (its range reaches into the tile from before, or
+  // starts at its first key tile), then b, b + 1, ... while they start in it
+  int slots[kMaxParts];
+  int n_parts = 0;
+  slots[n_parts++] = start(b - 1) >= t0 ? 2 * (b - 1) : 2 * (b - 1) + 1;
+  for (int g = b; g < sk.groups && n_parts < kMaxParts; ++g) {
+    const long long sg = start(g);
+    if (sg >= t1) break;
+    if (start(g + 1) > sg) slots[n_parts++] = 2 * g;     // a group with no work has no part
   }
-  const float inv = 1.0f / wsum;
-  uint2 out;
-  out.x = pack_bf16x2(o[0] * inv, o[1] * inv);
-  out.y = pack_bf16x2(o[2] * inv, o[3] * inv);
-  *(uint2*)(Og + L.out_off(bh) + (long long)row * L.on + c) = out;
-  if (LSEg != nullptr && c == 0) LSEg[(size_t)bh * N + row] = (mx + __log2f(wsum)) * 0.6931471805599453f;
+  const int bh = tile / n_qtiles, qt = tile - bh * n_qtiles;
+  const int c = (threadIdx.x & 31) * 4;
+#pragma unroll 4
+  for (int rr = 0; rr < kStreamKMergeRows / 8; ++rr) {
+    const int r = chunk * kStreamKMergeRows + rr * 8 + (threadIdx.x >> 5);
+    const int row = qt * BR + r;
+    if (row >= N) break;
+    float mx = -INFINITY;
+    for (int i = 0; i < n_parts; ++i) mx = fmaxf(mx, sk.ws_lse[(size_t)slots[i] * BR + r]);
+    float wsum = 0.f;
+    f32x4_t o = {0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < n_parts; ++i) {
+      const size_t idx = (size_t)slots[i] * BR + r;
+      const float w = fast_exp2(sk.ws_lse[idx] - mx);
+      wsum += w;
+      o += w * *(const f32x4_t*)(sk.ws_o + idx * D + c);
+    }
+    const float inv = 1.0f / wsum;
+    uint2 out;
+    out.x = pack_bf16x2(o[0] * inv, o[1] * inv);
+    out.y = pack_bf16x2(o[2] * inv, o[3] * inv);
+    *(uint2*)(Og + L.out_off(bh) + (long long)row * L.on + c) = out;
+    if (LSEg != nullptr && c == 0) LSEg[(size_t)bh * N + row] = (mx + __log2f(wsum)) * 0.6931471805599453f;
+  }
 }
 
 #undef DIT_FENCE

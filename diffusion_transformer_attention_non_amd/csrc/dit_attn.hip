@@ -213,7 +213,13 @@ int make_plan(int kind, long long BH, int N, int n_cu, int max_blocks, bool lse,
   constexpr int kD = CfgBf16D128::kD, kBR = CfgBf16D128::kBR;
   if (kind == kPlanBf16D128) {
     const int n_t = (N + 63) / 64;
-    const int groups = (int)std::min<long long>(n_cu, tiles * n_t / kStreamKMinKeyTiles);
+    // ranges of at least 4 key tiles, and long enough that a tile meets at
+    // most kStreamKMaxParts - 1 of them (the merge's limit): boundaries in a
+    // tile are a range apart, so a range of ceil(n_t / (max - 3)) key tiles
+    // puts at most max - 2 of them inside it
+    const long long min_range =
+        std::max<long long>(kStreamKMinKeyTiles, (n_t + kStreamKMaxParts - 4) / (kStreamKMaxParts - 3));
+    const int groups = (int)std::min<long long>(n_cu, tiles * n_t / min_range);
     PipeSplit alt;
     plan_split((int)tiles, 1, N, 64, n_cu, &alt);
     // Stream-K only up to two rounds of tiles: a CU's range then stays in
@@ -263,7 +269,8 @@ int launch_streamk(const void* q, const void* k, const void* v, void* o, float* 
                      L);
   hipError_t err = hipGetLastError();
   if (err == hipSuccess && groups > 1) {
-    hipLaunchKernelGGL(attn_streamk_combine_kernel, dim3((unsigned)((groups - 1) * (C::kBR / 8))), dim3(256), 0, st,
+    hipLaunchKernelGGL(attn_streamk_combine_kernel, dim3((unsigned)((groups - 1) * (C::kBR / kStreamKMergeRows))),
+                       dim3(256), 0, st,
                        static_cast<uint16_t*>(o), lse, N, n_qtiles, sk, L);
     err = hipGetLastError();
   }

@@ -88,7 +88,11 @@ def test_plan_invariants_over_shapes(n_cu):
             assert -(-p.split_tiles * p.parts // n_cu) < p.parts
         else:
             assert tiles <= 2 * n_cu
-            assert p.workgroups == min(n_cu, tiles * n_t // 4) and p.workgroups >= 2
+            min_range = max(4, -(-n_t // 13))
+            assert p.workgroups == min(n_cu, tiles * n_t // min_range) and p.workgroups >= 2
+            # the merge takes at most 16 parts of a cut tile: ranges are at least
+            # ceil(n_t / 13) key tiles, so at most 14 boundaries fall inside a tile
+            assert (tiles * n_t) // p.workgroups >= -(-n_t // 13)
             assert p.workspace_bytes == 2 * p.workgroups * 256 * ROW_BYTES
 
 
