@@ -333,13 +333,21 @@ __device__ __forceinline__ void pipe_tile(const uint16_t* __restrict__ Qg, const
   bf16x8_t pA[2][2], pB[2][2]; // P of two consecutive sub-tiles [query block][key half]
 
   // ---- prologue: K tiles u0..u0+2, V tiles u0, u0+1; the first sub-tile's
-  // logits and their exact row maxima
+  // logits and their exact row maxima. The first iteration reads K u0, K u0+1
+  // and V u0 only, so K u0+2 and V u0+1 go last and stay in flight (their 10
+  // instructions) until that iteration's own wait; the Q loads, issued before
+  // all of them, are complete once those are the only ones left.
   dma_tile(Kh, ktile(u0), kslot(u0), kdo);
-  if (u0 + 1 < u1) dma_tile(Kh, ktile(u0 + 1), kslot(u0 + 1), kdo);
-  if (u0 + 2 < u1) dma_tile(Kh, ktile(u0 + 2), kslot(u0 + 2), kdo);
   dma_tile(Vh, ktile(u0), vslot(u0), vdo);
-  if (u0 + 1 < u1) dma_tile(Vh, ktile(u0 + 1), vslot(u0 + 1), vdo);
-  __builtin_amdgcn_s_waitcnt(0x0F70);      // vmcnt(0)
+  if (u0 + 1 < u1) dma_tile(Kh, ktile(u0 + 1), kslot(u0 + 1), kdo);
+  if (u0 + 2 < u1) {
+    dma_tile(Kh, ktile(u0 + 2), kslot(u0 + 2), kdo);
+    dma_tile(Vh, ktile(u0 + 1), vslot(u0 + 1), vdo);
+    __builtin_amdgcn_s_waitcnt(0x0F7A);    // vmcnt(10)
+  } else {
+    if (u0 + 1 < u1) dma_tile(Vh, ktile(u0 + 1), vslot(u0 + 1), vdo);
+    __builtin_amdgcn_s_waitcnt(0x0F70);    // vmcnt(0)
+  }
   __syncthreads();
   read_kfrags(2 * u0);
   {
