@@ -39,6 +39,14 @@
 // recomputes the sub-tile's logits from K (still in LDS), takes their exact
 // maximum, rescales O and l and recomputes P. The row sums are of the
 // unrounded probabilities, so the log-sum-exp is the exact one.
+//
+// Schedules. pipe_tile runs one query tile over a range of key tiles.
+// attn_fwd_bf16_pipe_kernel gives each workgroup a whole tile, or one key
+// range of a tile of the last, partly filled round (merged afterwards by
+// attn_split_combine_kernel); attn_fwd_bf16_streamk_kernel gives each of one
+// workgroup per CU an equal contiguous range of (tile, key tile) pairs
+// (merged by attn_streamk_combine_kernel). The SPARSE form takes its key
+// tiles from a per-tile list instead of 0 .. n_t - 1.
 // Layout conventions (S^T = K Q^T, O^T = V^T P^T, V^T by transpose reads)
 // are those of attn_fwd_bf16.h. Built with -mllvm -amdgpu-mfma-vgpr-form.
 #pragma once
