@@ -517,17 +517,17 @@ void attn_fwd_fp8_pipe_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __r
           smfma(s0[st >> 1], st >> 1, 0, st & 1);          // block 0 (consumed in phase X)
           if (st == 0) rs0 = psum(pout[0]);
         } else if (st < 6) {
-          soft_step(s1, st, nm1, pout[1], ls1);            // key block 0 of S_j block 1 is free after
-          smfma(s1[0], 0, 1, st - 4);                      // words 0-3 (steps 0-3)
+          // words 4-7 of S_j block 1 by step 5, two a step: key block 0 is
+          // free after words 0-3 (steps 0-3), key block 1 after these
+          soft_step(s1, st, nm1, pout[1], ls1);
+          soft_step(s1, st + 2, nm1, pout[1], ls1);
+          smfma(s1[0], 0, 1, st - 4);
         } else if (st == 6) {
-          soft_step(s1, 6, nm1, pout[1], ls1);
-          soft_step(s1, 7, nm1, pout[1], ls1);
-          smfma(s1[1], 1, 1, 0);
-        } else {
-          // ahead of the last S MFMA, so that the sums are ready when the
-          // range test reads them
+          // two S MFMAs ahead of the range test that reads these sums
           rs1 = psum(pout[1]);
           DIT_FENCE();
+          smfma(s1[1], 1, 1, 0);
+        } else {
           smfma(s1[1], 1, 1, 1);
         }
         if (st < 4) soft_step(s1, st, nm1, pout[1], ls1);
