@@ -131,7 +131,8 @@ def main(argv=None):
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this library has no multi-GPU path "
-              "(every (b, h) slice is independent; sharding is described in DESIGN.md). "
+              "(every (b, h) slice is independent, so heads or batch entries shard across GPUs with no "
+              "exchange inside attention). "
               "Run with --gpus 1.", file=sys.stderr)
         return 2
 
