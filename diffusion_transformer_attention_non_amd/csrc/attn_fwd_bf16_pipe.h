@@ -71,6 +71,10 @@ struct PipeCfg {
   static constexpr int kVBase = kKSlots * kSlot;
   static constexpr int kLdsBytes = kVBase + kVSlots * kSlot;   // 143360
   static_assert(kKTile <= kSlot && kVTile <= kSlot, "tile fits its slot");
+  // The bf16 O rows of a finished tile are staged in LDS (over the K/V slots,
+  // 64 rows per wave, padded pitch) on their way to HBM.
+  static constexpr int kORow = 272;
+  static_assert(kNW * 64 * kORow <= kLdsBytes, "O staging fits the slots");
 };
 
 constexpr float kPipeSumLimit = 0x1p64f;   // overflow guard: far below FLT_MAX / N
@@ -584,26 +588,45 @@ __device__ __forceinline__ void pipe_tile(const uint16_t* __restrict__ Qg, const
     }
     return;
   }
+  // O goes to HBM through LDS. In the MFMA layout a lane holds 8-byte pieces
+  // of 32 different rows, so a direct store instruction touches 32 rows and
+  // the memory pipeline takes it one cache line at a time; staged, each store
+  // instruction writes 4 whole rows (1 KB, contiguous for packed rows). The
+  // staging reuses the K/V slots: no DMA is in flight after the last
+  // iteration, and the barrier waits until every wave has read its last
+  // fragments. Each wave stages and reads back only its own 64 rows.
+  __syncthreads();
+  char* ost = smem + wave * (64 * C::kORow);
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     const float l_tot = pair_sum(l_run[qb]);
     const float inv = 1.0f / l_tot;
+    char* srow = ost + (qb * 32 + l32) * C::kORow;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int d0 = db * 32 + i * 8 + hh * 4;
+        uint2 w;
+        w.x = pack_bf16x2(acc[qb][db][i * 4 + 0] * inv, acc[qb][db][i * 4 + 1] * inv);
+        w.y = pack_bf16x2(acc[qb][db][i * 4 + 2] * inv, acc[qb][db][i * 4 + 3] * inv);
+        *(uint2*)(srow + d0 * 2) = w;
+      }
     const int row = q0 + qb * 32 + l32;
-    if (row < N) {
-      uint16_t* orow = Og + obase + (long long)row * L.on;
+    if (LSEg != nullptr && hh == 0 && row < N)
+      LSEg[(size_t)bh * N + row] = (mc[qb] + __log2f(l_tot)) * 0.6931471805599453f;
+  }
+  // the staged rows are read by other lanes of the same wave: LDS operations
+  // of one wave complete in order, and the wait keeps the compiler from
+  // moving the reads above the writes
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  const int chunk = lane & 15;
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int d0 = db * 32 + i * 8 + hh * 4;
-          uint2 w;
-          w.x = pack_bf16x2(acc[qb][db][i * 4 + 0] * inv, acc[qb][db][i * 4 + 1] * inv);
-          w.y = pack_bf16x2(acc[qb][db][i * 4 + 2] * inv, acc[qb][db][i * 4 + 3] * inv);
-          *(uint2*)(orow + d0) = w;
-        }
-      if (LSEg != nullptr && hh == 0)
-        LSEg[(size_t)bh * N + row] = (mc[qb] + __log2f(l_tot)) * 0.6931471805599453f;
-    }
+  for (int r = 0; r < 16; ++r) {
+    const int rl = r * 4 + (lane >> 4);
+    const i32x4_t x = *(const i32x4_t*)(ost + rl * C::kORow + chunk * 16);
+    const int row = q0 + rl;
+    if (row < N) *(i32x4_t*)(Og + obase + (long long)row * L.on + chunk * 8) = x;
   }
 }
 

@@ -56,6 +56,8 @@ struct Fp8PipeCfg {
   static constexpr int kVBase = kKSlots * kSlot;
   static constexpr int kLdsBytes = kVBase + kVSlots * kSlot;   // 143360
   static_assert(kKTile <= kSlot && kVTile <= kSlot, "tile fits its slot");
+  static constexpr int kORow = 272;                        // O staging pitch, as in the bf16 kernel
+  static_assert(kNW * 64 * kORow <= kLdsBytes, "O staging fits the slots");
 };
 
 constexpr float kFp8PipePLog2 = 1.0f;          // P is scaled by 2 before the cast
@@ -701,27 +703,43 @@ void attn_fwd_fp8_pipe_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __r
     }
     return;
   }
+  // O goes to HBM through LDS, over the K/V slots (no DMA is in flight after
+  // the last iteration), so that each store instruction writes 4 whole rows
+  // instead of 8-byte pieces of 32 rows; each wave stages its own 64 rows.
+  __syncthreads();
+  char* ost = smem + wave * (64 * C::kORow);
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     const float l_tot = l_q[qb];
     const float mul = dv / l_tot;
-    const float l_exact = EXACT_LSE ? pair_sum(l_ex[qb]) : 0.f;
-    const int row = q0 + qb * 32 + l32;
-    if (row < N) {
-      uint16_t* orow = Og + obase + (long long)row * L.on;
+    char* srow = ost + (qb * 32 + l32) * C::kORow;
 #pragma unroll
-      for (int db = 0; db < 4; ++db)
+    for (int db = 0; db < 4; ++db)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int d0 = db * 32 + i * 8 + hh * 4;
-          uint2 w;
-          w.x = pack_bf16x2(acc[qb][db][i * 4 + 0] * mul, acc[qb][db][i * 4 + 1] * mul);
-          w.y = pack_bf16x2(acc[qb][db][i * 4 + 2] * mul, acc[qb][db][i * 4 + 3] * mul);
-          *(uint2*)(orow + d0) = w;
-        }
-      if (EXACT_LSE && hh == 0)
+      for (int i = 0; i < 4; ++i) {
+        const int d0 = db * 32 + i * 8 + hh * 4;
+        uint2 w;
+        w.x = pack_bf16x2(acc[qb][db][i * 4 + 0] * mul, acc[qb][db][i * 4 + 1] * mul);
+        w.y = pack_bf16x2(acc[qb][db][i * 4 + 2] * mul, acc[qb][db][i * 4 + 3] * mul);
+        *(uint2*)(srow + d0 * 2) = w;
+      }
+    if constexpr (EXACT_LSE) {
+      const float l_exact = pair_sum(l_ex[qb]);
+      const int row = q0 + qb * 32 + l32;
+      if (hh == 0 && row < N)
         LSEg[(size_t)bh * N + row] = (mc[qb] + __log2f(l_exact) - kFp8PipePLog2) * 0.6931471805599453f;
     }
+  }
+  // other lanes of the same wave read the staged rows: one wave's LDS
+  // operations complete in order, and the wait pins the reads after the writes
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  const int chunk = lane & 15;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int rl = r * 4 + (lane >> 4);
+    const i32x4_t x = *(const i32x4_t*)(ost + rl * C::kORow + chunk * 16);
+    const int row = q0 + rl;
+    if (row < N) *(i32x4_t*)(Og + obase + (long long)row * L.on + chunk * 8) = x;
   }
 }
 
