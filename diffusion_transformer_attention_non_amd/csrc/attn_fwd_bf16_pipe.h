@@ -75,6 +75,8 @@ struct PipeCfg {
   // 64 rows per wave, padded pitch) on their way to HBM.
   static constexpr int kORow = 272;
   static_assert(kNW * 64 * kORow <= kLdsBytes, "O staging fits the slots");
+  static constexpr int kWsRow = 528;                       // fp32 partial rows of a split tile
+  static_assert(kNW * 64 * kWsRow <= kLdsBytes, "partial-row staging fits the slots");
 };
 
 constexpr float kPipeSumLimit = 0x1p64f;   // overflow guard: far below FLT_MAX / N
@@ -567,14 +569,23 @@ __device__ __forceinline__ void pipe_tile(const uint16_t* __restrict__ Qg, const
       for (int qb = 0; qb < 2; ++qb)
         acc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[half][db], pA[qb][half], acc[qb][db], 0, 0, 0);
 
+  // The results go to memory through LDS. In the MFMA layout a lane holds
+  // pieces of 32 different rows, so a direct store instruction touches 32 rows
+  // and the memory pipeline takes it one cache line at a time; staged, each
+  // store instruction writes whole rows (1 KB). The staging reuses the K/V
+  // slots: no DMA is in flight after the last iteration, and the barrier waits
+  // until every wave has read its last fragments. Each wave stages and reads
+  // back only its own 64 rows; one wave's LDS operations complete in order, and
+  // the waits keep the compiler from moving the reads above the writes.
+  __syncthreads();
   if (ws_index >= 0) {
     // one key range of a split tile: fp32 rows normalised over the range
+    char* wst = smem + wave * (64 * C::kWsRow);
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       const float l_tot = pair_sum(l_run[qb]);
       const float inv = 1.0f / l_tot;
-      const int r = wave * 64 + qb * 32 + l32;
-      float* orow = split.ws_o + ((size_t)ws_index * C::kBR + r) * D;
+      char* srow = wst + (qb * 32 + l32) * C::kWsRow;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -582,20 +593,20 @@ __device__ __forceinline__ void pipe_tile(const uint16_t* __restrict__ Qg, const
           const int d0 = db * 32 + i * 8 + hh * 4;
           f32x4_t w = {acc[qb][db][i * 4 + 0] * inv, acc[qb][db][i * 4 + 1] * inv, acc[qb][db][i * 4 + 2] * inv,
                        acc[qb][db][i * 4 + 3] * inv};
-          *(f32x4_t*)(orow + d0) = w;
+          *(f32x4_t*)(srow + d0 * 4) = w;
         }
-      if (hh == 0) split.ws_lse[(size_t)ws_index * C::kBR + r] = mc[qb] + __log2f(l_tot);
+      if (hh == 0) split.ws_lse[(size_t)ws_index * C::kBR + wave * 64 + qb * 32 + l32] = mc[qb] + __log2f(l_tot);
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    float* wrows = split.ws_o + ((size_t)ws_index * C::kBR + wave * 64) * D;
+    const int c32 = lane & 31;
+#pragma unroll
+    for (int r = 0; r < 32; ++r) {
+      const int rl = r * 2 + (lane >> 5);
+      *(f32x4_t*)(wrows + rl * D + c32 * 4) = *(const f32x4_t*)(wst + rl * C::kWsRow + c32 * 16);
     }
     return;
   }
-  // O goes to HBM through LDS. In the MFMA layout a lane holds 8-byte pieces
-  // of 32 different rows, so a direct store instruction touches 32 rows and
-  // the memory pipeline takes it one cache line at a time; staged, each store
-  // instruction writes 4 whole rows (1 KB, contiguous for packed rows). The
-  // staging reuses the K/V slots: no DMA is in flight after the last
-  // iteration, and the barrier waits until every wave has read its last
-  // fragments. Each wave stages and reads back only its own 64 rows.
-  __syncthreads();
   char* ost = smem + wave * (64 * C::kORow);
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
@@ -616,9 +627,6 @@ __device__ __forceinline__ void pipe_tile(const uint16_t* __restrict__ Qg, const
     if (LSEg != nullptr && hh == 0 && row < N)
       LSEg[(size_t)bh * N + row] = (mc[qb] + __log2f(l_tot)) * 0.6931471805599453f;
   }
-  // the staged rows are read by other lanes of the same wave: LDS operations
-  // of one wave complete in order, and the wait keeps the compiler from
-  // moving the reads above the writes
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   const int chunk = lane & 15;
 #pragma unroll
