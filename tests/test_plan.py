@@ -113,3 +113,30 @@ def test_plan_for_the_current_device_needs_one():
     if torch.cuda.is_available():
         pytest.skip("a GPU is present")
     assert dit.dit_attn_plan(1, 1, 64, 128, BF16, 0, 0, 0)[0] == dit.DIT_ATTN_EDEVICE
+
+
+@pytest.mark.parametrize("n_cu", [80, 256, 304])
+def test_streamk_ranges_cover_each_pair_once_and_cut_tiles_into_at_most_16_parts(n_cu):
+    """The stream-K kernel gives group g the pairs [work*g/G, work*(g+1)/G)
+    (integer division) and its merge handles at most 16 parts of one tile;
+    for every stream-K plan over the shapes below, the ranges tile the
+    (tile, key tile) pairs exactly and no tile meets more than 16 ranges."""
+    seen = 0
+    for B, H in itertools.product([1, 2], [1, 2, 3, 4, 5, 6, 8]):
+        for N in [64, 300, 2048, 4608, 12800, 16896, 25088, 40001]:
+            p = plan(B, H, N, n_cu=n_cu)
+            if p.schedule != STREAMK:
+                continue
+            seen += 1
+            tiles, n_t, G = B * H * -(-N // 256), -(-N // 64), p.workgroups
+            work = tiles * n_t
+            bounds = [work * g // G for g in range(G + 1)]
+            assert bounds[0] == 0 and bounds[-1] == work
+            assert all(b1 > b0 for b0, b1 in zip(bounds, bounds[1:]))       # no empty range
+            parts = [0] * tiles
+            for g in range(G):
+                first, last = bounds[g] // n_t, (bounds[g + 1] - 1) // n_t
+                for t in range(first, last + 1):
+                    parts[t] += 1
+            assert max(parts) <= 16, (B, H, N, n_cu, max(parts))
+    assert seen >= 5
