@@ -5,11 +5,18 @@ default workload, B=1, H=24, N=16896 (512 text + 128x128 image tokens),
 d=128, bf16 in and out. Inputs are resident in HBM before timing starts.
 
 Prints ONE JSON line. ``value`` is TFLOP/s by 4*B*H*N^2*d over the wall
-clock of K back-to-back steps (synchronised on both sides). ``roofline``
-uses the per-launch kernel time from events recorded on the stream the
-kernel runs on. ``cpu_baseline`` times the fp64 CPU oracle on a bounded
-sample of query rows of the same workload (each output row depends on one
-query row, so a row sample is the same computation, only fewer rows).
+clock of K back-to-back steps (synchronised on both sides), each step one
+call of the library with a caller-owned workspace (the schedule that splits
+the last round of query tiles along the keys). ``roofline`` uses the
+per-launch kernel time from events recorded on the stream the kernel runs
+on. ``cpu_baseline`` times the fp64 CPU oracle on every row of the same
+workload (or, with --cpu-rows, on a row sample: each output row depends on
+one query row, so a sample is the same computation, only fewer rows), and
+``check`` compares the output of the last timed step with that oracle.
+``clocks`` are the GPU's shader and memory clocks read by a child process
+(amd-smi) before and after the timed work; ``cold`` times single calls after
+a 512 MiB scrub of the caches; ``no_workspace`` times the short entry point
+dit_attn_fwd, which runs one workgroup per query tile.
 ``fp8``, ``fp8_mx`` and ``blocksparse`` are companion figures of the same
 workload: the e4m3 path with per-tensor scales, the e4m3 path with one scale
 per 32 values (scaled MFMA), and block-sparse attention over the text key
@@ -74,8 +81,9 @@ def time_launches(fn, warmup: int, steps: int):
     return wall, per
 
 
-def cpu_baseline(q, k, v, scale, budget_s: float):
-    """Time the fp64 oracle on a bounded row sample; return its TFLOP/s."""
+def cpu_baseline(q, k, v, scale, max_rows: int = 0):
+    """Time the fp64 oracle over batch entry 0 (every batch entry when B > 1
+    and every row is asked for); return (record, rows, oracle output)."""
     import numpy as np
     import oracle
     try:
@@ -85,18 +93,14 @@ def cpu_baseline(q, k, v, scale, budget_s: float):
     except Exception:
         threads = len(os.sched_getaffinity(0))
     B, H, N, d = q.shape
-    q64, k64, v64 = (t[:1].double().numpy() for t in (q, k, v))
-    # calibrate on 64 rows of every head of batch entry 0, then size the sample to the budget
-    rows = np.arange(64)
+    full = max_rows <= 0 or max_rows >= N
+    nb = B if full else 1
+    q64, k64, v64 = (t[:nb].double().numpy() for t in (q, k, v))
+    rows = np.arange(N) if full else np.linspace(0, N - 1, max_rows).astype(np.int64)
     t0 = time.perf_counter()
-    oracle.attention(q64, k64, v64, scale, rows=rows)
-    t_cal = time.perf_counter() - t0
-    n_rows = int(min(N, max(64, 64 * budget_s / max(t_cal, 1e-3))))
-    rows = np.linspace(0, N - 1, n_rows).astype(np.int64)
-    t0 = time.perf_counter()
-    oracle.attention(q64, k64, v64, scale, rows=rows)
+    o_ref, _ = oracle.attention(q64, k64, v64, scale, rows=rows)
     t = time.perf_counter() - t0
-    flops = 4.0 * H * n_rows * N * d
+    flops = 4.0 * nb * H * rows.size * N * d
     cpu = ""
     try:
         for line in open("/proc/cpuinfo"):
@@ -105,9 +109,62 @@ def cpu_baseline(q, k, v, scale, budget_s: float):
                 break
     except OSError:
         pass
-    return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"fp64 numpy oracle on {n_rows} of {N} query rows x {H} heads of batch entry 0 "
-                      f"({flops / 1e9:.1f} GFLOP in {t:.1f} s); host CPU: {cpu}"}
+    what = "every query row of the workload" if full else f"{rows.size} of {N} query rows x {H} heads of batch entry 0"
+    rec = {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+           "sample": f"fp64 numpy oracle on {what} ({flops / 1e9:.1f} GFLOP in {t:.1f} s); host CPU: {cpu}"}
+    return rec, rows, o_ref, nb
+
+
+def output_error(o_dev, o_ref, rows, nb):
+    """max / mean |O_gpu - O_oracle| over the rows the oracle computed."""
+    import numpy as np
+    import torch
+    idx = torch.as_tensor(rows, device=o_dev.device)
+    got = o_dev[:nb].index_select(2, idx).float().cpu().double().numpy()
+    err = np.abs(got - o_ref)
+    return {"max_abs": float(err.max()), "mean_abs": float(err.mean()), "elements": int(err.size)}
+
+
+def read_clocks():
+    """Current shader (sclk) and memory (mclk) clocks in MHz of GPU 0, read by
+    a child process; None where the tool is missing or prints no such field."""
+    import re
+    import subprocess
+    out = {"sclk_mhz": None, "mclk_mhz": None, "source": None}
+    for cmd in (["amd-smi", "metric", "-g", "0", "-c"], ["rocm-smi", "-d", "0", "--showclocks"]):
+        try:
+            text = subprocess.run(cmd, capture_output=True, text=True, timeout=30).stdout
+        except (OSError, subprocess.SubprocessError):
+            continue
+        if cmd[0] == "amd-smi":
+            # blocks "GFX_0:" / "MEM_0:" each followed by an indented "CLK: <n> MHz"
+            g = re.search(r"GFX_0:\s*\n\s*CLK:\s*([\d.]+)\s*MHz", text)
+            m = re.search(r"MEM_0:\s*\n\s*CLK:\s*([\d.]+)\s*MHz", text)
+        else:
+            g = re.search(r"sclk clock level:[^(]*\(([\d.]+)\s*Mhz\)", text, re.I)
+            m = re.search(r"mclk clock level:[^(]*\(([\d.]+)\s*Mhz\)", text, re.I)
+        if g or m:
+            out.update(sclk_mhz=float(g.group(1)) if g else None, mclk_mhz=float(m.group(1)) if m else None,
+                       source=cmd[0])
+            break
+    return out
+
+
+def time_cold(fn, steps: int, scrub_mib: int = 512):
+    """Median per-call kernel ms with a scrub of scrub_mib MiB written between calls."""
+    import torch
+    scrub = torch.empty(scrub_mib << 20, dtype=torch.uint8, device="cuda")
+    per = []
+    for i in range(steps):
+        scrub.fill_(i & 0xFF)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        torch.cuda.synchronize()
+        per.append(a.elapsed_time(b))
+    del scrub
+    return statistics.median(per)
 
 
 def main(argv=None):
@@ -122,8 +179,11 @@ def main(argv=None):
     ap.add_argument("--layout", choices=["bhnd", "bnhd"], default="bhnd",
                     help="rows of q, k, v and o packed as [B][H][N][d] (default) or taken from [B][N][H][d] "
                          "buffers through dit_attn_fwd_strided")
-    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
+    ap.add_argument("--cpu-rows", type=int, default=0,
+                    help="query rows per head for cpu_baseline (0: every row of the workload)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the clock readings, the cold-cache and the no-workspace companion timings")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB three times (to calibrate "
                          "the FETCH_SIZE / WRITE_SIZE counters against known bytes) and exit")
@@ -164,17 +224,21 @@ def main(argv=None):
     stream = torch.cuda.current_stream()
     handle = stream.cuda_stream
     in_strides, out_strides = qd.stride()[:3], od.stride()[:3]
+    # the caller-owned workspace, sized by the plan (allocated before timing)
+    ws_bytes = max(dit.workspace_bytes(B, H, N, d, dit.DIT_ATTN_BF16),
+                   dit.workspace_bytes(B, H, N, d, dit.DIT_ATTN_FP8_E4M3))
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    _, plan = dit.dit_attn_plan(B, H, N, d, dit.DIT_ATTN_BF16, 0, False, 0, ws_bytes)
+    clocks_before = None if args.no_extras else read_clocks()
 
     def step():
-        if args.layout == "bnhd":
-            st = dit.dit_attn_fwd_strided(qd, kd, vd, od, B, H, N, d, scale, dit.DIT_ATTN_BF16, in_strides,
-                                          out_strides, None, None, handle)
-        else:
-            st = dit.dit_attn_fwd(qd, kd, vd, od, B, H, N, d, scale, dit.DIT_ATTN_BF16, handle)
+        st = dit.dit_attn_fwd_strided(qd, kd, vd, od, B, H, N, d, scale, dit.DIT_ATTN_BF16, in_strides,
+                                      out_strides, None, None, ws, ws_bytes, handle)
         if st != 0:
-            raise dit.DitAttnError(st, "dit_attn_fwd")
+            raise dit.DitAttnError(st, "dit_attn_fwd_strided")
 
     wall, per = time_launches(step, args.warmup, args.steps)
+    o_timed = od.clone()
     flops = w.flops
     ms_per_step = wall / args.steps * 1e3
     value = flops / (wall / args.steps) / 1e12
@@ -188,7 +252,8 @@ def main(argv=None):
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic: Q, K, V iid N(0,1) rounded to bf16, seed 0",
         "config": {"workload": w.name, "B": B, "H": H, "N": N, "d": d, "n_text": w.n_text,
-                   "n_image": w.n_image, "causal": False, "scale": scale, "layout": args.layout},
+                   "n_image": w.n_image, "causal": False, "scale": scale, "layout": args.layout,
+                   "schedule": ["tile", "split", "stream-k"][plan.schedule], "workspace_bytes": ws_bytes},
         "pct_of_peak": round(100.0 * value / peak, 2),
         "kernel_ms": {"mean": round(k_mean, 4), "median": round(statistics.median(per), 4),
                       "p95": round(sorted(per)[int(0.95 * (len(per) - 1))], 4), "min": round(min(per), 4)},
@@ -207,11 +272,12 @@ def main(argv=None):
 
         def step8():
             st = dit.dit_attn_fwd_strided(q8, k8, v8, od, B, H, N, d, scale, dit.DIT_ATTN_FP8_E4M3,
-                                          q8.stride()[:3], out_strides, descale, None, handle)
+                                          q8.stride()[:3], out_strides, descale, None, ws, ws_bytes, handle)
             if st != 0:
                 raise dit.DitAttnError(st, "dit_attn_fwd_strided")
 
         wall8, per8 = time_launches(step8, args.warmup, args.steps)
+        o8_timed = od.clone()
         v8_tflops = flops / (wall8 / args.steps) / 1e12
         k8_mean = statistics.fmean(per8)
         line["fp8"] = {"workload": w.name + "_fp8", "value": round(v8_tflops, 2), "unit": "TFLOP/s",
@@ -228,7 +294,7 @@ def main(argv=None):
         vm, vsc = dit.quantize_mx(vd, "tokens")
 
         def step_mx():
-            st = dit.dit_attn_fwd_mx(qm, km, vm, qsc, ksc, vsc, od, B, H, N, d, scale, None, handle)
+            st = dit.dit_attn_fwd_mx(qm, km, vm, qsc, ksc, vsc, od, B, H, N, d, scale, None, ws, ws_bytes, handle)
             if st != 0:
                 raise dit.DitAttnError(st, "dit_attn_fwd_mx")
 
@@ -244,6 +310,8 @@ def main(argv=None):
     if args.sparse_density > 0 and args.layout == "bhnd" and d == 128:
         from workloads import random_kv_blocks
         blocks, counts = random_kv_blocks(B, H, N, args.sparse_density, seed=w.seed)
+        ws_sparse = dit.workspace_bytes(B, H, N, d, dit.DIT_ATTN_BF16, max_blocks=blocks.shape[-1])
+        ws_s = torch.empty(max(ws_sparse, 16), dtype=torch.uint8, device=dev)
         # keys each query row visits, summed over rows (the listed blocks' real sizes)
         nq, mb = counts.shape[-1], blocks.shape[-1]
         visited = 0
@@ -256,7 +324,7 @@ def main(argv=None):
 
         def step_sparse():
             st = dit.dit_attn_fwd_blocksparse(qd, kd, vd, od, B, H, N, d, scale, dit.DIT_ATTN_BF16, blocks_d,
-                                              counts_d, mb, None, None, None, handle)
+                                              counts_d, mb, None, None, None, ws_s, ws_sparse, handle)
             if st != 0:
                 raise dit.DitAttnError(st, "dit_attn_fwd_blocksparse")
 
@@ -273,8 +341,34 @@ def main(argv=None):
                          "unit": "TFLOP/s", "frac": round(sflops / (ks_mean * 1e-3) / 1e12 / peak, 4),
                          "traffic": None}}
 
+    if not args.no_extras:
+        clocks_after = read_clocks()
+        line["clocks"] = {"before": clocks_before, "after": clocks_after}
+
+        def step_short():
+            st = dit.dit_attn_fwd(qd, kd, vd, od, B, H, N, d, scale, dit.DIT_ATTN_BF16, handle)
+            if st != 0:
+                raise dit.DitAttnError(st, "dit_attn_fwd")
+
+        if args.layout == "bhnd":
+            walln, pern = time_launches(step_short, args.warmup, args.steps)
+            line["no_workspace"] = {"entry_point": "dit_attn_fwd", "schedule": "tile",
+                                    "value": round(flops / (walln / args.steps) / 1e12, 2), "unit": "TFLOP/s",
+                                    "kernel_ms_mean": round(statistics.fmean(pern), 4)}
+        cold = time_cold(step, min(args.steps, 10))
+        line["cold"] = {"scrub_mib": 512, "kernel_ms_median": round(cold, 4),
+                        "value": round(flops / (cold * 1e-3) / 1e12, 2), "unit": "TFLOP/s"}
+
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(q, k, v, scale, args.cpu_budget)
+        rec, rows, o_ref, nb = cpu_baseline(q, k, v, scale, args.cpu_rows)
+        line["cpu_baseline"] = rec
+        check = {"bf16": output_error(o_timed, o_ref, rows, nb), "spec_max_abs": 2e-2, "spec_mean_abs": 2e-3}
+        check["bf16"]["within_spec"] = check["bf16"]["max_abs"] <= 2e-2 and check["bf16"]["mean_abs"] <= 2e-3
+        if "fp8" in line:
+            check["fp8"] = output_error(o8_timed, o_ref, rows, nb)
+            check["fp8"]["within_spec"] = check["fp8"]["max_abs"] <= 6e-2
+            check["spec_max_abs_fp8"] = 6e-2
+        line["check"] = check
     line["context"] = ("pages (NVIDIA B200, FLUX 3 Image Klein, 2048x2048): Base text-to-image denoise "
                        "14.24 s of 14.70 s; dense BF16 attention ~60% of DiT kernel time")
     print(json.dumps(line), flush=True)

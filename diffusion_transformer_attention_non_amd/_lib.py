@@ -18,6 +18,7 @@ DIT_ATTN_EINVAL = -1
 DIT_ATTN_EUNSUPPORTED = -2
 DIT_ATTN_EDEVICE = -3
 DIT_ATTN_ELAUNCH = -4
+DIT_ATTN_EWORKSPACE = -5
 
 DIT_ATTN_SPARSE_Q_BLOCK = 256
 DIT_ATTN_SPARSE_KV_BLOCK = 64
@@ -36,7 +37,9 @@ EXPORTED = ("dit_attn_fwd", "dit_attn_fwd_blocksparse", "dit_attn_fwd_ex", "dit_
 class DitAttnPlan(ctypes.Structure):
     """dit_attn_plan_t."""
     _fields_ = [("schedule", ctypes.c_int32), ("workgroups", ctypes.c_int32), ("parts", ctypes.c_int32),
-                ("split_tiles", ctypes.c_int32), ("workspace_bytes", ctypes.c_int64)]
+                ("split_tiles", ctypes.c_int32), ("workspace_bytes", ctypes.c_int64),
+                ("workspace_wanted", ctypes.c_int64), ("best_schedule", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is not built; run `python -m diffusion_transformer_attention_non_amd.build` "
@@ -48,16 +51,17 @@ _lib.dit_attn_fwd.argtypes = [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _vp]
 _lib.dit_attn_fwd.restype = _i
 _lib.dit_attn_fwd_ex.argtypes = [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _vp, _vp, _vp]
 _lib.dit_attn_fwd_ex.restype = _i
-_lib.dit_attn_fwd_strided.argtypes = [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _vp, _vp, _vp, _vp, _vp]
+_lib.dit_attn_fwd_strided.argtypes = [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _vp, _vp, _vp, _vp, _vp, _i64,
+                                      _vp]
 _lib.dit_attn_fwd_strided.restype = _i
 _lib.dit_attn_fwd_blocksparse.argtypes = [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _vp, _vp, _i,
-                                          _vp, _vp, _vp, _vp]
+                                          _vp, _vp, _vp, _vp, _i64, _vp]
 _lib.dit_attn_fwd_blocksparse.restype = _i
-_lib.dit_attn_fwd_mx.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _vp, _vp]
+_lib.dit_attn_fwd_mx.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _vp, _vp, _i64, _vp]
 _lib.dit_attn_fwd_mx.restype = _i
 _lib.dit_attn_quantize_mx.argtypes = [_vp, _i, _i, _i, _i, _i, _vp, _vp, _vp]
 _lib.dit_attn_quantize_mx.restype = _i
-_lib.dit_attn_plan.argtypes = [_i, _i, _i, _i, _i, _i, _i, _i, ctypes.POINTER(DitAttnPlan)]
+_lib.dit_attn_plan.argtypes = [_i, _i, _i, _i, _i, _i, _i, _i, _i64, ctypes.POINTER(DitAttnPlan)]
 _lib.dit_attn_plan.restype = _i
 _lib.dit_attn_quantize_e4m3.argtypes = [_vp, _i64, _vp, _vp, _vp, _vp]
 _lib.dit_attn_quantize_e4m3.restype = _i
@@ -94,35 +98,39 @@ def _strides3(s):
 
 
 def dit_attn_fwd_strided(q, k, v, o, B, H, N, d, scale, dtype, qkv_strides=None, o_strides=None,
-                         descale_qkv=None, lse=None, stream=None) -> int:
+                         descale_qkv=None, lse=None, workspace=None, workspace_bytes=0, stream=None) -> int:
     qs, qp = _strides3(qkv_strides)
     os_, op = _strides3(o_strides)
     return _lib.dit_attn_fwd_strided(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, H, N, d, scale, dtype, qp, op,
-                                     _ptr(descale_qkv), _ptr(lse), _ptr(stream))
+                                     _ptr(descale_qkv), _ptr(lse), _ptr(workspace), int(workspace_bytes),
+                                     _ptr(stream))
 
 
 def dit_attn_fwd_blocksparse(q, k, v, o, B, H, N, d, scale, dtype, kv_blocks, kv_counts, max_blocks,
-                             qkv_strides=None, o_strides=None, lse=None, stream=None) -> int:
+                             qkv_strides=None, o_strides=None, lse=None, workspace=None, workspace_bytes=0,
+                             stream=None) -> int:
     qs, qp = _strides3(qkv_strides)
     os_, op = _strides3(o_strides)
     return _lib.dit_attn_fwd_blocksparse(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, H, N, d, scale, dtype,
                                          _ptr(kv_blocks), _ptr(kv_counts), max_blocks, qp, op, _ptr(lse),
-                                         _ptr(stream))
+                                         _ptr(workspace), int(workspace_bytes), _ptr(stream))
 
 
-def dit_attn_fwd_mx(q8, k8, v8, q_scales, k_scales, v_scales, o, B, H, N, d, scale, lse=None, stream=None) -> int:
+def dit_attn_fwd_mx(q8, k8, v8, q_scales, k_scales, v_scales, o, B, H, N, d, scale, lse=None, workspace=None,
+                    workspace_bytes=0, stream=None) -> int:
     return _lib.dit_attn_fwd_mx(_ptr(q8), _ptr(k8), _ptr(v8), _ptr(q_scales), _ptr(k_scales), _ptr(v_scales), _ptr(o),
-                                B, H, N, d, scale, _ptr(lse), _ptr(stream))
+                                B, H, N, d, scale, _ptr(lse), _ptr(workspace), int(workspace_bytes), _ptr(stream))
 
 
 def dit_attn_quantize_mx(x, B, H, N, d, along, x8, scales, stream=None) -> int:
     return _lib.dit_attn_quantize_mx(_ptr(x), B, H, N, d, along, _ptr(x8), _ptr(scales), _ptr(stream))
 
 
-def dit_attn_plan(B, H, N, d, dtype, max_blocks=0, lse=False, n_cu=0):
+def dit_attn_plan(B, H, N, d, dtype, max_blocks=0, lse=False, n_cu=0, workspace_bytes=0):
     """Returns (status, DitAttnPlan)."""
     plan = DitAttnPlan()
-    st = _lib.dit_attn_plan(B, H, N, d, dtype, max_blocks, 1 if lse else 0, n_cu, ctypes.byref(plan))
+    st = _lib.dit_attn_plan(B, H, N, d, dtype, max_blocks, 1 if lse else 0, n_cu, int(workspace_bytes),
+                            ctypes.byref(plan))
     return st, plan
 
 

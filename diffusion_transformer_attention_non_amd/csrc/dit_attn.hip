@@ -153,7 +153,9 @@ int launch_bf16(const void* q, const void* k, const void* v, void* o, float* lse
 // prologue and epilogue), with at least 4 key tiles per range and at most
 // kMaxSplitRows partial rows. parts = 1 (no split) when nothing is gained.
 constexpr double kPartOverhead = 2.0;
-constexpr long long kMaxSplitRows = 1 << 18;     // 256 Ki rows x 129 floats = 135 MB
+// Partial rows of one call, split or stream-K: 128 Ki rows x 129 floats =
+// 67.6 MB (+ 0.5 MB of exact LSE sums for fp8 with an LSE output).
+constexpr long long kMaxSplitRows = 1 << 17;
 
 int plan_split(int BH, int n_qtiles, int N, int key_tile, int n_cu, PipeSplit* sp) {
   const int tiles = BH * n_qtiles;
@@ -201,6 +203,8 @@ struct Plan {
   long long workgroups;  // of the attention kernel
   size_t units;          // partial rows in the workspace
   size_t ws_floats;      // workspace size in floats
+  int best_schedule;     // the fastest schedule (what a large enough workspace buys)
+  size_t wanted_floats;  // its workspace size in floats
 };
 
 int make_plan(int kind, long long BH, int N, int n_cu, int max_blocks, bool lse, Plan* p) {
@@ -208,7 +212,8 @@ int make_plan(int kind, long long BH, int N, int n_cu, int max_blocks, bool lse,
   const long long n_qtiles = (N + br - 1) / br;
   const long long tiles = n_qtiles * BH;
   if (tiles > 0x7fffffffLL / 8) return DIT_ATTN_EINVAL;
-  *p = Plan{DIT_ATTN_SCHED_TILE, PipeSplit{(int)tiles, 0, 1, nullptr, nullptr, nullptr}, 0, tiles, 0, 0};
+  *p = Plan{DIT_ATTN_SCHED_TILE, PipeSplit{(int)tiles, 0, 1, nullptr, nullptr, nullptr}, 0, tiles, 0, 0,
+            DIT_ATTN_SCHED_TILE, 0};
   if (kind == kPlanBf16D64) return DIT_ATTN_OK;
   constexpr int kD = CfgBf16D128::kD, kBR = CfgBf16D128::kBR;
   if (kind == kPlanBf16D128) {
@@ -219,7 +224,8 @@ int make_plan(int kind, long long BH, int N, int n_cu, int max_blocks, bool lse,
     // puts at most max - 2 of them inside it
     const long long min_range =
         std::max<long long>(kStreamKMinKeyTiles, (n_t + kStreamKMaxParts - 4) / (kStreamKMaxParts - 3));
-    const int groups = (int)std::min<long long>(n_cu, tiles * n_t / min_range);
+    const int groups = (int)std::min<long long>(std::min<long long>(n_cu, kMaxSplitRows / (2 * kBR)),
+                                                tiles * n_t / min_range);
     PipeSplit alt;
     plan_split((int)tiles, 1, N, 64, n_cu, &alt);
     // Stream-K only up to two rounds of tiles: a CU's range then stays in
@@ -249,19 +255,35 @@ int make_plan(int kind, long long BH, int N, int n_cu, int max_blocks, bool lse,
   return DIT_ATTN_OK;
 }
 
-// Dense bf16 d = 128 under stream-K: `groups` workgroups, partial rows in a
-// stream-ordered workspace of 2 groups slots, merged by the combine kernel.
-// Returns 1 if it launched (status in *status), 0 if the workspace could not
-// be had (the caller then runs the split plan).
+// The plan of a call given `ws_bytes` of caller workspace: the fastest
+// schedule if the workspace holds its partial rows, one workgroup per tile
+// if no workspace is given, DIT_ATTN_EWORKSPACE for a workspace that is given
+// but too small (a caller that passes one expects it to be used).
+int resolve_plan(int kind, long long BH, int N, int n_cu, int max_blocks, bool lse, int64_t ws_bytes, Plan* p) {
+  if (ws_bytes < 0) return DIT_ATTN_EINVAL;
+  const int st = make_plan(kind, BH, N, n_cu, max_blocks, lse, p);
+  if (st != DIT_ATTN_OK) return st;
+  p->best_schedule = p->schedule;
+  p->wanted_floats = p->ws_floats;
+  const uint64_t need = (uint64_t)p->ws_floats * sizeof(float);
+  if (need == 0 || (uint64_t)ws_bytes >= need) return DIT_ATTN_OK;
+  if (ws_bytes != 0) return DIT_ATTN_EWORKSPACE;
+  const long long tiles = p->sp.n_full + (long long)p->sp.n_split;
+  p->schedule = DIT_ATTN_SCHED_TILE;
+  p->sp = PipeSplit{(int)tiles, 0, 1, nullptr, nullptr, nullptr};
+  p->groups = 0;
+  p->workgroups = tiles;
+  p->units = 0;
+  p->ws_floats = 0;
+  return DIT_ATTN_OK;
+}
+
+// Dense bf16 d = 128 under stream-K: `groups` workgroups, partial rows in the
+// workspace's 2 groups slots, merged by the combine kernel.
 template <class C>
 int launch_streamk(const void* q, const void* k, const void* v, void* o, float* lse, int tiles, int N,
-                   int n_qtiles, float scale_log2, hipStream_t st, int groups, const Layout& L, int* status) {
+                   int n_qtiles, float scale_log2, hipStream_t st, int groups, const Layout& L, void* ws) {
   const size_t units = (size_t)2 * groups * C::kBR;
-  void* ws = nullptr;
-  if (hipMallocAsync(&ws, units * (C::kD + 1) * sizeof(float), st) != hipSuccess || ws == nullptr) {
-    (void)hipGetLastError();
-    return 0;
-  }
   StreamK sk{static_cast<float*>(ws), static_cast<float*>(ws) + units * C::kD, groups, tiles};
   hipLaunchKernelGGL(attn_fwd_bf16_streamk_kernel<C>, dim3((unsigned)groups), dim3(C::kThreads), C::kLdsBytes, st,
                      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
@@ -274,40 +296,25 @@ int launch_streamk(const void* q, const void* k, const void* v, void* o, float* 
                        static_cast<uint16_t*>(o), lse, N, n_qtiles, sk, L);
     err = hipGetLastError();
   }
-  (void)hipFreeAsync(ws, st);
-  *status = err == hipSuccess ? DIT_ATTN_OK : DIT_ATTN_ELAUNCH;
-  return 1;
+  return err == hipSuccess ? DIT_ATTN_OK : DIT_ATTN_ELAUNCH;
 }
 
 // SPARSE: block lists in kvb; the split planner then takes max_blocks as
-// the key-tile count (the host never reads the lists).
+// the key-tile count (the host never reads the lists). `plan` comes from
+// resolve_plan; ws holds its partial rows (unused without them).
 template <class C, bool SPARSE = false>
 int launch_pipe(const void* q, const void* k, const void* v, void* o, float* lse, int BH, int N,
-                float scale, hipStream_t st, int n_cu, const Layout& L, const KvBlocks& kvb = KvBlocks{}) {
-  Plan plan;
-  const int pst = make_plan(SPARSE ? kPlanBf16D128Sparse : kPlanBf16D128, BH, N, n_cu, kvb.max_blocks, lse != nullptr,
-                            &plan);
-  if (pst != DIT_ATTN_OK) return pst;
+                float scale, hipStream_t st, const Plan& plan, void* ws, const Layout& L,
+                const KvBlocks& kvb = KvBlocks{}) {
   const int n_qtiles = (N + C::kBR - 1) / C::kBR;
   const int tiles = n_qtiles * BH;
   const float scale_log2 = scale * 1.4426950408889634f;
-  if (plan.schedule == DIT_ATTN_SCHED_STREAMK) {
-    int status = DIT_ATTN_OK;
-    if (launch_streamk<C>(q, k, v, o, lse, tiles, N, n_qtiles, scale_log2, st, plan.groups, L, &status)) return status;
-    // no workspace: the split plan without its workspace is one workgroup per tile
-    plan.schedule = DIT_ATTN_SCHED_TILE;
-  }
-  PipeSplit sp = PipeSplit{tiles, 0, 1, nullptr, nullptr, nullptr};
-  void* ws = nullptr;
+  if (plan.schedule == DIT_ATTN_SCHED_STREAMK)
+    return launch_streamk<C>(q, k, v, o, lse, tiles, N, n_qtiles, scale_log2, st, plan.groups, L, ws);
+  PipeSplit sp = plan.sp;
   if (plan.schedule == DIT_ATTN_SCHED_SPLIT) {
-    if (hipMallocAsync(&ws, plan.ws_floats * sizeof(float), st) == hipSuccess && ws != nullptr) {
-      sp = plan.sp;
-      sp.ws_o = static_cast<float*>(ws);
-      sp.ws_lse = sp.ws_o + plan.units * C::kD;
-    } else {
-      (void)hipGetLastError();
-      ws = nullptr;
-    }
+    sp.ws_o = static_cast<float*>(ws);
+    sp.ws_lse = sp.ws_o + plan.units * C::kD;
   }
   const long long grid = (long long)sp.n_full + (long long)sp.n_split * sp.parts;
   auto* kernel = &attn_fwd_bf16_pipe_kernel<C, SPARSE>;
@@ -316,13 +323,10 @@ int launch_pipe(const void* q, const void* k, const void* v, void* o, float* lse
                      static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), lse, N, n_qtiles,
                      scale_log2, scale, sp, L, kvb);
   hipError_t err = hipGetLastError();
-  if (ws != nullptr) {
-    if (err == hipSuccess) {
-      hipLaunchKernelGGL(attn_split_combine_kernel, dim3((unsigned)(sp.n_split * (C::kBR / 8))), dim3(256), 0, st,
-                         sp.ws_o, sp.ws_lse, static_cast<uint16_t*>(o), lse, N, n_qtiles, sp, L);
-      err = hipGetLastError();
-    }
-    (void)hipFreeAsync(ws, st);
+  if (err == hipSuccess && plan.schedule == DIT_ATTN_SCHED_SPLIT) {
+    hipLaunchKernelGGL(attn_split_combine_kernel, dim3((unsigned)(sp.n_split * (C::kBR / 8))), dim3(256), 0, st,
+                       sp.ws_o, sp.ws_lse, static_cast<uint16_t*>(o), lse, N, n_qtiles, sp, L);
+    err = hipGetLastError();
   }
   return err == hipSuccess ? DIT_ATTN_OK : DIT_ATTN_ELAUNCH;
 }
@@ -330,27 +334,16 @@ int launch_pipe(const void* q, const void* k, const void* v, void* o, float* lse
 // MX: block-scaled inputs with their scales in mxs (descale unused)
 template <class C, bool MX = false>
 int launch_fp8(const void* q, const void* k, const void* v, void* o, float* lse, const float* descale,
-               int BH, int N, float scale, hipStream_t st, int n_cu, const Layout& L,
+               int BH, int N, float scale, hipStream_t st, const Plan& plan, void* ws, const Layout& L,
                const MxScales& mxs = MxScales{nullptr, nullptr, nullptr}) {
   static_assert(C::kBR == PipeCfg::kBR && C::kD == PipeCfg::kD, "the merge kernel assumes 256 x 128 tiles");
-  Plan plan;
-  const int pst = make_plan(kPlanFp8D128, BH, N, n_cu, 0, lse != nullptr, &plan);
-  if (pst != DIT_ATTN_OK) return pst;
   const int n_qtiles = (N + C::kBR - 1) / C::kBR;
-  const int tiles = n_qtiles * BH;
   const float scale_log2 = scale * 1.4426950408889634f;
-  PipeSplit sp = PipeSplit{tiles, 0, 1, nullptr, nullptr, nullptr};
-  void* ws = nullptr;
+  PipeSplit sp = plan.sp;
   if (plan.schedule == DIT_ATTN_SCHED_SPLIT) {
-    if (hipMallocAsync(&ws, plan.ws_floats * sizeof(float), st) == hipSuccess && ws != nullptr) {
-      sp = plan.sp;
-      sp.ws_o = static_cast<float*>(ws);
-      sp.ws_lse = sp.ws_o + plan.units * C::kD;
-      sp.ws_lse_out = lse != nullptr ? sp.ws_lse + plan.units : nullptr;
-    } else {
-      (void)hipGetLastError();
-      ws = nullptr;
-    }
+    sp.ws_o = static_cast<float*>(ws);
+    sp.ws_lse = sp.ws_o + plan.units * C::kD;
+    sp.ws_lse_out = lse != nullptr ? sp.ws_lse + plan.units : nullptr;
   }
   const long long grid = (long long)sp.n_full + (long long)sp.n_split * sp.parts;
   auto* kernel = lse != nullptr ? &attn_fwd_fp8_pipe_kernel<C, true, MX> : &attn_fwd_fp8_pipe_kernel<C, false, MX>;
@@ -359,13 +352,10 @@ int launch_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
                      static_cast<const uint8_t*>(v), static_cast<uint16_t*>(o), lse, descale, N, n_qtiles,
                      scale_log2, scale, sp, L, mxs);
   hipError_t err = hipGetLastError();
-  if (ws != nullptr) {
-    if (err == hipSuccess) {
-      hipLaunchKernelGGL(attn_split_combine_kernel, dim3((unsigned)(sp.n_split * (C::kBR / 8))), dim3(256), 0, st,
-                         sp.ws_o, sp.ws_lse, static_cast<uint16_t*>(o), lse, N, n_qtiles, sp, L);
-      err = hipGetLastError();
-    }
-    (void)hipFreeAsync(ws, st);
+  if (err == hipSuccess && plan.schedule == DIT_ATTN_SCHED_SPLIT) {
+    hipLaunchKernelGGL(attn_split_combine_kernel, dim3((unsigned)(sp.n_split * (C::kBR / 8))), dim3(256), 0, st,
+                       sp.ws_o, sp.ws_lse, static_cast<uint16_t*>(o), lse, N, n_qtiles, sp, L);
+    err = hipGetLastError();
   }
   return err == hipSuccess ? DIT_ATTN_OK : DIT_ATTN_ELAUNCH;
 }
@@ -418,11 +408,30 @@ int check_call(const void* q, const void* k, const void* v, void* o, int B, int 
   return DIT_ATTN_OK;
 }
 
+// A workspace of ws_bytes > 0 must be a 16-byte aligned pointer that overlaps
+// none of the n buffers (pointer, byte span; NULL pointers are skipped).
+// ws_bytes == 0 means no workspace, whatever the pointer.
+int check_workspace(const void* ws, int64_t ws_bytes, const void* const* bufs, const uint64_t* spans, int n) {
+  if (ws_bytes < 0) return DIT_ATTN_EINVAL;
+  if (ws_bytes == 0) return DIT_ATTN_OK;
+  if (ws == nullptr || !aligned(ws, 16)) return DIT_ATTN_EINVAL;
+  for (int i = 0; i < n; ++i)
+    if (bufs[i] != nullptr && overlap(ws, (uint64_t)ws_bytes, bufs[i], spans[i])) return DIT_ATTN_EINVAL;
+  return DIT_ATTN_OK;
+}
+
+int plan_kind(int d, int dtype, int max_blocks) {
+  return dtype == DIT_ATTN_FP8_E4M3 ? kPlanFp8D128
+         : d == 64                  ? kPlanBf16D64
+         : max_blocks > 0           ? kPlanBf16D128Sparse
+                                    : kPlanBf16D128;
+}
+
 }  // namespace
 
 extern "C" {
 
-int dit_attn_version(void) { return (1 << 16) | 4; }
+int dit_attn_version(void) { return (2 << 16) | 0; }
 
 const char* dit_attn_strerror(int status) {
   switch (status) {
@@ -431,30 +440,39 @@ const char* dit_attn_strerror(int status) {
     case DIT_ATTN_EUNSUPPORTED: return "unsupported head dimension or dtype";
     case DIT_ATTN_EDEVICE: return "no gfx950 HIP device is current";
     case DIT_ATTN_ELAUNCH: return "kernel launch failed";
+    case DIT_ATTN_EWORKSPACE: return "workspace smaller than the call's plan needs";
     default: return "unknown status";
   }
 }
 
 int dit_attn_fwd_strided(const void* q, const void* k, const void* v, void* o, int B, int H, int N, int d,
                          float scale, int dtype, const int64_t* qkv_strides, const int64_t* o_strides,
-                         const float* descale_qkv, float* lse, void* stream) {
+                         const float* descale_qkv, float* lse, void* workspace, int64_t workspace_bytes,
+                         void* stream) {
   Checked c;
   const int status = check_call(q, k, v, o, B, H, N, d, scale, dtype, qkv_strides, o_strides, descale_qkv, lse, &c);
   if (status != DIT_ATTN_OK) return status;
+  const void* bufs[5] = {q, k, v, o, lse};
+  const uint64_t spans[5] = {c.in_bytes, c.in_bytes, c.in_bytes, c.out_bytes, c.lse_bytes};
+  const int ws_status = check_workspace(workspace, workspace_bytes, bufs, spans, 5);
+  if (ws_status != DIT_ATTN_OK) return ws_status;
   const int dev_status = check_device();
   if (dev_status != DIT_ATTN_OK) return dev_status;
+  Plan plan;
+  const int pst = resolve_plan(plan_kind(d, dtype, 0), c.bh, N, cu_count(), 0, lse != nullptr, workspace_bytes, &plan);
+  if (pst != DIT_ATTN_OK) return pst;
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (dtype == DIT_ATTN_BF16) {
-    if (d == 128) return launch_pipe<CfgBf16D128>(q, k, v, o, lse, c.bh, N, scale, st, cu_count(), c.L);
+    if (d == 128) return launch_pipe<CfgBf16D128>(q, k, v, o, lse, c.bh, N, scale, st, plan, workspace, c.L);
     return launch_bf16<CfgBf16D64>(q, k, v, o, lse, c.bh, N, scale, st, c.L);
   }
-  return launch_fp8<CfgFp8D128>(q, k, v, o, lse, descale_qkv, c.bh, N, scale, st, cu_count(), c.L);
+  return launch_fp8<CfgFp8D128>(q, k, v, o, lse, descale_qkv, c.bh, N, scale, st, plan, workspace, c.L);
 }
 
 int dit_attn_fwd_blocksparse(const void* q, const void* k, const void* v, void* o, int B, int H, int N, int d,
                              float scale, int dtype, const int32_t* kv_blocks, const int32_t* kv_counts,
                              int max_blocks, const int64_t* qkv_strides, const int64_t* o_strides, float* lse,
-                             void* stream) {
+                             void* workspace, int64_t workspace_bytes, void* stream) {
   Checked c;
   const int status = check_call(q, k, v, o, B, H, N, d, scale, dtype, qkv_strides, o_strides, nullptr, lse, &c);
   if (status != DIT_ATTN_OK) return status;
@@ -471,17 +489,26 @@ int dit_attn_fwd_blocksparse(const void* q, const void* k, const void* v, void* 
     return DIT_ATTN_EINVAL;
   if (lse && (overlap(lse, c.lse_bytes, kv_blocks, list_bytes) || overlap(lse, c.lse_bytes, kv_counts, count_bytes)))
     return DIT_ATTN_EINVAL;
+  const void* bufs[7] = {q, k, v, o, lse, kv_blocks, kv_counts};
+  const uint64_t spans[7] = {c.in_bytes, c.in_bytes, c.in_bytes, c.out_bytes, c.lse_bytes, list_bytes, count_bytes};
+  const int ws_status = check_workspace(workspace, workspace_bytes, bufs, spans, 7);
+  if (ws_status != DIT_ATTN_OK) return ws_status;
   const int dev_status = check_device();
   if (dev_status != DIT_ATTN_OK) return dev_status;
+  Plan plan;
+  const int pst =
+      resolve_plan(kPlanBf16D128Sparse, c.bh, N, cu_count(), max_blocks, lse != nullptr, workspace_bytes, &plan);
+  if (pst != DIT_ATTN_OK) return pst;
   using C = CfgBf16D128;
   static_assert(C::kBR == DIT_ATTN_SPARSE_Q_BLOCK, "query block = the kernel's query tile");
   const KvBlocks kvb{kv_blocks, kv_counts, max_blocks};
-  return launch_pipe<C, true>(q, k, v, o, lse, c.bh, N, scale, static_cast<hipStream_t>(stream), cu_count(), c.L,
-                              kvb);
+  return launch_pipe<C, true>(q, k, v, o, lse, c.bh, N, scale, static_cast<hipStream_t>(stream), plan, workspace,
+                              c.L, kvb);
 }
 
-int dit_attn_plan(int B, int H, int N, int d, int dtype, int max_blocks, int lse, int n_cu, dit_attn_plan_t* plan) {
-  if (!plan || B < 1 || H < 1 || N < 1 || n_cu < 0 || max_blocks < 0) return DIT_ATTN_EINVAL;
+int dit_attn_plan(int B, int H, int N, int d, int dtype, int max_blocks, int lse, int n_cu, int64_t workspace_bytes,
+                  dit_attn_plan_t* plan) {
+  if (!plan || B < 1 || H < 1 || N < 1 || n_cu < 0 || max_blocks < 0 || workspace_bytes < 0) return DIT_ATTN_EINVAL;
   if (dtype != DIT_ATTN_BF16 && dtype != DIT_ATTN_FP8_E4M3) return DIT_ATTN_EUNSUPPORTED;
   if (dtype == DIT_ATTN_BF16 && d != 64 && d != 128) return DIT_ATTN_EUNSUPPORTED;
   if (dtype == DIT_ATTN_FP8_E4M3 && d != 128) return DIT_ATTN_EUNSUPPORTED;
@@ -494,24 +521,24 @@ int dit_attn_plan(int B, int H, int N, int d, int dtype, int max_blocks, int lse
     if (dev_status != DIT_ATTN_OK) return dev_status;
     n_cu = cu_count();
   }
-  const int kind = dtype == DIT_ATTN_FP8_E4M3 ? kPlanFp8D128
-                   : d == 64                  ? kPlanBf16D64
-                   : max_blocks > 0           ? kPlanBf16D128Sparse
-                                              : kPlanBf16D128;
   Plan p;
-  const int st = make_plan(kind, bh, N, n_cu, max_blocks, lse != 0, &p);
+  const int st = resolve_plan(plan_kind(d, dtype, max_blocks), bh, N, n_cu, max_blocks, lse != 0, workspace_bytes, &p);
   if (st != DIT_ATTN_OK) return st;
   plan->schedule = p.schedule;
   plan->workgroups = (int32_t)p.workgroups;
   plan->parts = p.schedule == DIT_ATTN_SCHED_SPLIT ? p.sp.parts : 1;
   plan->split_tiles = p.schedule == DIT_ATTN_SCHED_SPLIT ? p.sp.n_split : 0;
   plan->workspace_bytes = (int64_t)(p.ws_floats * sizeof(float));
+  plan->workspace_wanted = (int64_t)(p.wanted_floats * sizeof(float));
+  plan->best_schedule = p.best_schedule;
+  plan->reserved = 0;
   return DIT_ATTN_OK;
 }
 
 int dit_attn_fwd_ex(const void* q, const void* k, const void* v, void* o, int B, int H, int N, int d,
                     float scale, int dtype, const float* descale_qkv, float* lse, void* stream) {
-  return dit_attn_fwd_strided(q, k, v, o, B, H, N, d, scale, dtype, nullptr, nullptr, descale_qkv, lse, stream);
+  return dit_attn_fwd_strided(q, k, v, o, B, H, N, d, scale, dtype, nullptr, nullptr, descale_qkv, lse, nullptr, 0,
+                              stream);
 }
 
 int dit_attn_fwd(const void* q, const void* k, const void* v, void* o, int B, int H, int N, int d, float scale,
@@ -520,7 +547,8 @@ int dit_attn_fwd(const void* q, const void* k, const void* v, void* o, int B, in
 }
 
 int dit_attn_fwd_mx(const void* q8, const void* k8, const void* v8, const void* q_scales, const void* k_scales,
-                    const void* v_scales, void* o, int B, int H, int N, int d, float scale, float* lse, void* stream) {
+                    const void* v_scales, void* o, int B, int H, int N, int d, float scale, float* lse,
+                    void* workspace, int64_t workspace_bytes, void* stream) {
   Checked c;
   const int status = check_call(q8, k8, v8, o, B, H, N, d, scale, DIT_ATTN_FP8_E4M3, nullptr, nullptr, nullptr, lse, &c);
   if (status != DIT_ATTN_OK) return status;
@@ -534,12 +562,19 @@ int dit_attn_fwd_mx(const void* q8, const void* k8, const void* v8, const void* 
     if (overlap(o, c.out_bytes, sc[i], sb[i])) return DIT_ATTN_EINVAL;
     if (lse && overlap(lse, c.lse_bytes, sc[i], sb[i])) return DIT_ATTN_EINVAL;
   }
+  const void* bufs[8] = {q8, k8, v8, o, lse, q_scales, k_scales, v_scales};
+  const uint64_t spans[8] = {c.in_bytes, c.in_bytes, c.in_bytes, c.out_bytes, c.lse_bytes, sb[0], sb[1], sb[2]};
+  const int ws_status = check_workspace(workspace, workspace_bytes, bufs, spans, 8);
+  if (ws_status != DIT_ATTN_OK) return ws_status;
   const int dev_status = check_device();
   if (dev_status != DIT_ATTN_OK) return dev_status;
+  Plan plan;
+  const int pst = resolve_plan(kPlanFp8D128, c.bh, N, cu_count(), 0, lse != nullptr, workspace_bytes, &plan);
+  if (pst != DIT_ATTN_OK) return pst;
   const MxScales mxs{static_cast<const uint8_t*>(q_scales), static_cast<const uint8_t*>(k_scales),
                      static_cast<const uint8_t*>(v_scales)};
   return launch_fp8<CfgFp8D128, true>(q8, k8, v8, o, lse, nullptr, c.bh, N, scale, static_cast<hipStream_t>(stream),
-                                      cu_count(), c.L, mxs);
+                                      plan, workspace, c.L, mxs);
 }
 
 int dit_attn_quantize_mx(const void* x, int B, int H, int N, int d, int along, void* x8, void* scales,

@@ -18,30 +18,33 @@
  * ---------------------------------------
  * Layout:    q, k, v, o are contiguous row-major [B][H][N][d] tensors, d
  *            innermost, in device memory. o is always bfloat16.
- * Ownership: the caller allocates, owns and frees every buffer it passes.
- *            One internal buffer exists: when a bf16 d = 128 call would leave
- *            the GPU's last round of workgroups partly filled, query tiles are
- *            split along the keys (the last round's tiles, or, for calls of at
- *            most two rounds, every CU taking an equal share of all (query
- *            tile, key tile) pairs) and their fp32 partial rows go to a
- *            stream-ordered scratch buffer (hipMallocAsync on `stream`,
- *            released by hipFreeAsync on `stream` after the merge; at most
- *            2 x CUs x 256 rows x 129 floats, 67.6 MB on a 256-CU MI355X). If
- *            that allocation fails the call runs without it, with the same
- *            result semantics. The library retains no memory, never synchronises,
- *            and keeps no state beyond its loaded code objects and a
- *            per-device record (gfx950 or not, CU count).
+ * Ownership: the caller allocates, owns and frees every buffer it passes,
+ *            and the library never allocates, frees or retains device or
+ *            host memory. Some shapes run faster with a workspace: when a
+ *            bf16 d = 128 or fp8 call would leave the GPU's last round of
+ *            workgroups partly filled, its query tiles are split along the
+ *            keys (the last round's tiles, or, for calls of at most two
+ *            rounds, every CU taking an equal share of all (query tile, key
+ *            tile) pairs) and the fp32 partial rows are merged afterwards.
+ *            Those rows live in a caller-owned workspace, passed to the
+ *            entry points that take one and sized by dit_attn_plan (at most
+ *            2^17 partial rows of 129 floats, plus 2^17 floats for an fp8
+ *            call with an LSE output: 68.2 MB).
+ *            Without a workspace (the short forms dit_attn_fwd and
+ *            dit_attn_fwd_ex, or a NULL workspace) the call runs one
+ *            workgroup per query tile; dit_attn_plan reports which schedule
+ *            a call takes. The library keeps no state beyond its loaded code
+ *            objects and a per-device record (gfx950 or not, CU count).
  * Streams:   work is enqueued on `stream` (a hipStream_t; NULL = the null
  *            stream) and the call returns at once. The calls contain no host
- *            synchronisation or device-to-host read. Under HIP graph capture
- *            the scratch buffer above becomes a stream-ordered allocation;
- *            that case is not tested.
+ *            synchronisation, device-to-host read, allocation or memset, so
+ *            they can be captured in a HIP graph (kernel nodes only).
  * Errors:    every entry point returns DIT_ATTN_OK or a negative status, and
  *            launches nothing when it returns an error other than
  *            DIT_ATTN_ELAUNCH. Faults inside a kernel are not seen by the
  *            call; the caller sees them when it synchronises the stream.
  * Threads:   re-entrant; any number of host threads may call on their own
- *            streams.
+ *            streams. Calls that overlap in time must not share a workspace.
  */
 #ifndef DIT_ATTN_H
 #define DIT_ATTN_H
@@ -68,7 +71,8 @@ enum {
     DIT_ATTN_EINVAL = -1,        /* NULL / misaligned / aliasing pointer, B, H or N < 1, bad scale, size overflow */
     DIT_ATTN_EUNSUPPORTED = -2,  /* head dimension or dtype not implemented */
     DIT_ATTN_EDEVICE = -3,       /* no HIP device, or the current device is not gfx950 */
-    DIT_ATTN_ELAUNCH = -4        /* the kernel launch itself failed */
+    DIT_ATTN_ELAUNCH = -4,       /* the kernel launch itself failed */
+    DIT_ATTN_EWORKSPACE = -5     /* a workspace was given but is smaller than the call's plan needs */
 };
 
 /*
@@ -85,6 +89,10 @@ enum {
  * scale   : logit multiplier (1/sqrt(d) for standard attention); finite, > 0.
  * dtype   : a dit_attn_dtype_t value.
  * stream  : hipStream_t or NULL.
+ *
+ * Runs without a workspace: one workgroup per query tile. The same call
+ * through dit_attn_fwd_strided (NULL strides) with a workspace takes the
+ * faster schedules that split query tiles along the keys.
  *
  * Status: DIT_ATTN_EINVAL, _EUNSUPPORTED or _EDEVICE before any launch;
  * DIT_ATTN_ELAUNCH if hipLaunchKernel reports an error.
@@ -124,11 +132,22 @@ DIT_ATTN_API int dit_attn_fwd_ex(const void* q, const void* k, const void* v, vo
  * aliasing checks of dit_attn_fwd use the byte spans the strides cover. lse
  * stays packed as [B][H][N]. Other arguments and statuses as for
  * dit_attn_fwd_ex (DIT_ATTN_EINVAL for a stride that breaks these rules).
+ *
+ * workspace       : device memory owned by the caller, 16-byte aligned, or
+ *                   NULL. Must not overlap q, k, v, o or lse. Its contents on
+ *                   entry do not matter and are undefined afterwards; calls
+ *                   in flight at the same time need their own.
+ * workspace_bytes : its size. 0 (with any pointer): run without a workspace,
+ *                   one workgroup per query tile. Otherwise it must be at
+ *                   least dit_attn_plan's workspace_wanted for this shape
+ *                   (else DIT_ATTN_EWORKSPACE and nothing is launched), and
+ *                   the call takes the plan's fastest schedule.
  */
 DIT_ATTN_API int dit_attn_fwd_strided(const void* q, const void* k, const void* v, void* o,
                          int B, int H, int N, int d, float scale, int dtype,
                          const int64_t* qkv_strides, const int64_t* o_strides,
-                         const float* descale_qkv, float* lse, void* stream);
+                         const float* descale_qkv, float* lse,
+                         void* workspace, int64_t workspace_bytes, void* stream);
 
 /* Tile sizes of dit_attn_fwd_blocksparse: query rows per list, keys per listed block. */
 #define DIT_ATTN_SPARSE_Q_BLOCK 256
@@ -161,20 +180,21 @@ DIT_ATTN_API int dit_attn_fwd_strided(const void* q, const void* k, const void* 
  * max_blocks : row length of kv_blocks, 1 <= max_blocks <= ceil(N/64).
  * Neither list may overlap o or lse; they may share memory with q, k, v.
  * Only dtype = DIT_ATTN_BF16 with d = 128 is implemented (else
- * DIT_ATTN_EUNSUPPORTED). The last, partly filled round of workgroups is
- * split as in dit_attn_fwd, over list positions instead of key tiles (the
- * planner takes max_blocks as the list length, as the host never reads the
- * lists), with the same stream-ordered scratch buffer.
- * Other arguments, layouts (qkv_strides, o_strides may be NULL) and statuses
- * as for dit_attn_fwd_strided. A list that breaks the rules above cannot
- * make the kernel access memory outside q, k, v, o, lse and the lists (a
- * block index out of range reads zero rows), but its result is unspecified.
+ * DIT_ATTN_EUNSUPPORTED). With a workspace, the last, partly filled round of
+ * workgroups is split as in dit_attn_fwd_strided, over list positions
+ * instead of key tiles (the planner takes max_blocks as the list length, as
+ * the host never reads the lists). The workspace must not overlap the lists
+ * either. Other arguments, layouts (qkv_strides, o_strides may be NULL),
+ * workspace rules and statuses as for dit_attn_fwd_strided. A list that
+ * breaks the rules above cannot make the kernel access memory outside q, k,
+ * v, o, lse, the lists and the workspace (a block index out of range reads
+ * zero rows), but its result is unspecified.
  */
 DIT_ATTN_API int dit_attn_fwd_blocksparse(const void* q, const void* k, const void* v, void* o,
                              int B, int H, int N, int d, float scale, int dtype,
                              const int32_t* kv_blocks, const int32_t* kv_counts, int max_blocks,
                              const int64_t* qkv_strides, const int64_t* o_strides,
-                             float* lse, void* stream);
+                             float* lse, void* workspace, int64_t workspace_bytes, void* stream);
 
 /* Block axis of dit_attn_quantize_mx. */
 #define DIT_ATTN_MX_ALONG_D 0       /* 32 consecutive d values of a row (Q, K) */
@@ -202,11 +222,14 @@ DIT_ATTN_API int dit_attn_fwd_blocksparse(const void* q, const void* k, const vo
  *              16-byte aligned.
  * o, lse, B, H, N, scale, stream: as for dit_attn_fwd_ex. d must be 128
  * (else DIT_ATTN_EUNSUPPORTED). o and lse must not overlap any input or
- * scale array. Statuses as for dit_attn_fwd_ex.
+ * scale array. workspace, workspace_bytes: as for dit_attn_fwd_strided (it
+ * must not overlap the scale arrays either); the plan is that of a
+ * DIT_ATTN_FP8_E4M3 call. Statuses as for dit_attn_fwd_strided.
  */
 DIT_ATTN_API int dit_attn_fwd_mx(const void* q8, const void* k8, const void* v8,
                     const void* q_scales, const void* k_scales, const void* v_scales, void* o,
-                    int B, int H, int N, int d, float scale, float* lse, void* stream);
+                    int B, int H, int N, int d, float scale, float* lse,
+                    void* workspace, int64_t workspace_bytes, void* stream);
 
 /*
  * dit_attn_quantize_mx - block-scaled e4m3 quantisation of a bf16 tensor.
@@ -256,36 +279,49 @@ DIT_ATTN_API int dit_attn_quantize_e4m3(const void* x, int64_t n, void* x8, floa
 #define DIT_ATTN_SCHED_STREAMK 2  /* every CU takes an equal share of (query tile, key tile) pairs */
 
 typedef struct {
-    int32_t schedule;         /* DIT_ATTN_SCHED_* */
+    int32_t schedule;         /* DIT_ATTN_SCHED_* the call takes with the workspace given */
     int32_t workgroups;       /* workgroups of the attention kernel */
     int32_t parts;            /* key ranges per split query tile (SPLIT), else 1 */
     int32_t split_tiles;      /* query tiles split along the keys (SPLIT), else 0 */
-    int64_t workspace_bytes;  /* stream-ordered scratch the call allocates and frees, 0 if none */
+    int64_t workspace_bytes;  /* workspace bytes that schedule uses, 0 if none */
+    int64_t workspace_wanted; /* workspace bytes of the fastest schedule, 0 if it needs none */
+    int32_t best_schedule;    /* DIT_ATTN_SCHED_* of the fastest schedule */
+    int32_t reserved;
 } dit_attn_plan_t;
 
 /*
  * dit_attn_plan - the schedule an attention call of this shape would use.
  *
- * The launch decides its schedule from the shape alone (never from the
- * data); this returns that decision without launching anything, so a caller
- * can size memory or check the plan. B, H, N, d, dtype as for dit_attn_fwd;
- * max_blocks > 0 describes a dit_attn_fwd_blocksparse call with that list
- * length (bf16, d = 128 only), 0 a dense call (the block-scaled fp8 call
- * plans as DIT_ATTN_FP8_E4M3); lse != 0 if an LSE output is requested.
- * n_cu: compute units to plan for; 0 means the current device's (then a
- * gfx950 device must be current, else DIT_ATTN_EDEVICE).
- * plan   : host pointer, filled on DIT_ATTN_OK.
- * Status: DIT_ATTN_EINVAL (NULL plan, sizes < 1, n_cu < 0, max_blocks out
- * of range), DIT_ATTN_EUNSUPPORTED (d, dtype), DIT_ATTN_EDEVICE.
+ * The launch decides its schedule from the shape and the workspace size
+ * alone (never from the data); this returns that decision without launching
+ * anything, so a caller can size the workspace or check the plan. B, H, N,
+ * d, dtype as for dit_attn_fwd; max_blocks > 0 describes a
+ * dit_attn_fwd_blocksparse call with that list length (bf16, d = 128 only),
+ * 0 a dense call (the block-scaled fp8 call plans as DIT_ATTN_FP8_E4M3);
+ * lse != 0 if an LSE output is requested.
+ * n_cu            : compute units to plan for; 0 means the current device's
+ *                   (then a gfx950 device must be current, else
+ *                   DIT_ATTN_EDEVICE).
+ * workspace_bytes : the workspace the call will be given (0: none, as for
+ *                   dit_attn_fwd and dit_attn_fwd_ex). A call without one
+ *                   reports schedule DIT_ATTN_SCHED_TILE and, in
+ *                   best_schedule / workspace_wanted, what a workspace would
+ *                   buy.
+ * plan            : host pointer, filled on DIT_ATTN_OK.
+ * Status: DIT_ATTN_EINVAL (NULL plan, sizes < 1, n_cu < 0, workspace_bytes
+ * < 0, max_blocks out of range), DIT_ATTN_EUNSUPPORTED (d, dtype),
+ * DIT_ATTN_EDEVICE, DIT_ATTN_EWORKSPACE (0 < workspace_bytes <
+ * workspace_wanted, as the call itself would return).
  */
 DIT_ATTN_API int dit_attn_plan(int B, int H, int N, int d, int dtype, int max_blocks, int lse, int n_cu,
-                  dit_attn_plan_t* plan);
+                  int64_t workspace_bytes, dit_attn_plan_t* plan);
 
 /* Human-readable name of a status code (static string, never NULL). */
 DIT_ATTN_API const char* dit_attn_strerror(int status);
 
-/* Library ABI version: (major << 16) | minor (1.1 adds dit_attn_fwd_strided,
-   1.2 dit_attn_fwd_blocksparse, 1.3 dit_attn_fwd_mx and dit_attn_quantize_mx, 1.4 dit_attn_plan). */
+/* Library ABI version: (major << 16) | minor. 2.0: caller-owned workspaces
+   (dit_attn_fwd_strided, _blocksparse and _mx take one; dit_attn_plan takes
+   its size and reports the schedule it buys); nothing allocates. */
 DIT_ATTN_API int dit_attn_version(void);
 
 #ifdef __cplusplus

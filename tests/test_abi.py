@@ -39,10 +39,11 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_strerror_and_version(lib):
-    assert lib.dit_attn_version() >> 16 == 1
-    for st in (0, -1, -2, -3, -4, 7):
+    assert lib.dit_attn_version() >> 16 == 2
+    for st in (0, -1, -2, -3, -4, -5, 7):
         assert isinstance(lib.dit_attn_strerror(st), str) and lib.dit_attn_strerror(st)
     assert lib.dit_attn_strerror(-2) != lib.dit_attn_strerror(-1)
+    assert "workspace" in lib.dit_attn_strerror(-5)
 
 
 A, B_, C, O = 0x10000, 0x20000, 0x30000, 0x40000   # fake, aligned, disjoint addresses (never dereferenced)
@@ -74,7 +75,7 @@ def test_fwd_rejects_bad_arguments_before_launch(lib, args, expect):
 
 def test_fwd_rejects_bad_arguments_strided_too(lib):
     for args, expect in [((0, B_, C, O, 1, 1, 8, 64, 0.125, 0), -1), ((A, B_, C, O, 1, 1, 8, 96, 0.125, 0), -2)]:
-        assert lib.dit_attn_fwd_strided(*args, None, None, None, None, None) == expect
+        assert lib.dit_attn_fwd_strided(*args, None, None, None, None, None, 0, None) == expect
 
 
 # (B, H, N, d) = (2, 3, 8, 64) bf16 at disjoint fake addresses 16 MiB apart
@@ -101,7 +102,7 @@ def test_strided_layout_checks(lib, qkv, o, expect, why):
     import torch
     if torch.cuda.is_available():
         pytest.skip("a GPU is present; layouts are run by the GPU tests")
-    st = lib.dit_attn_fwd_strided(SA, SB, SC, SO, 2, 3, 8, 64, 0.125, 0, qkv, o, None, None, None)
+    st = lib.dit_attn_fwd_strided(SA, SB, SC, SO, 2, 3, 8, 64, 0.125, 0, qkv, o, None, None, None, 0, None)
     assert st == expect, why
 
 
@@ -110,7 +111,8 @@ def test_strided_output_overlap_uses_the_span(lib):
     if torch.cuda.is_available():
         pytest.skip("a GPU is present")
     # o starts inside the span of a [B][N][H][d] v (v covers 2*8*3*64*2 bytes)
-    assert lib.dit_attn_fwd_strided(SA, SB, SC, SC + 4096, 2, 3, 8, 64, 0.125, 0, BNHD, None, None, None, None) == -1
+    assert lib.dit_attn_fwd_strided(SA, SB, SC, SC + 4096, 2, 3, 8, 64, 0.125, 0, BNHD, None, None, None, None, 0,
+                                    None) == -1
 
 
 # block-sparse: (B, H, N, d) = (1, 2, 1000, 128) bf16, 4 query blocks, 16 key blocks
@@ -138,7 +140,7 @@ def test_blocksparse_checks(lib, args, lists, expect, why):
     import torch
     if torch.cuda.is_available():
         pytest.skip("a GPU is present; the block-sparse path is run by the GPU tests")
-    assert lib.dit_attn_fwd_blocksparse(*args, *lists, None, None, None, None) == expect, why
+    assert lib.dit_attn_fwd_blocksparse(*args, *lists, None, None, None, None, 0, None) == expect, why
 
 
 def test_blocksparse_list_overlapping_lse(lib):
@@ -147,9 +149,9 @@ def test_blocksparse_list_overlapping_lse(lib):
         pytest.skip("a GPU is present")
     lse = 0x7000000
     args = (SA, SB, SC, SO, 1, 2, 1000, 128, 0.1, 0)
-    assert lib.dit_attn_fwd_blocksparse(*args, LB, LC, 16, None, None, lse, None) == -3
-    assert lib.dit_attn_fwd_blocksparse(*args, lse + 4000, LC, 16, None, None, lse, None) == -1
-    assert lib.dit_attn_fwd_blocksparse(*args, LB, lse + 8, 16, None, None, lse, None) == -1
+    assert lib.dit_attn_fwd_blocksparse(*args, LB, LC, 16, None, None, lse, None, 0, None) == -3
+    assert lib.dit_attn_fwd_blocksparse(*args, lse + 4000, LC, 16, None, None, lse, None, 0, None) == -1
+    assert lib.dit_attn_fwd_blocksparse(*args, LB, lse + 8, 16, None, None, lse, None, 0, None) == -1
 
 
 # MX: (B, H, N, d) = (1, 2, 100, 128); codes 25600 bytes, row scales 800, V scales 4 * 128 * 2 = 1024
@@ -170,7 +172,7 @@ def test_mx_attention_checks(lib, args, expect, why):
     import torch
     if torch.cuda.is_available():
         pytest.skip("a GPU is present")
-    assert lib.dit_attn_fwd_mx(*args) == expect, why
+    assert lib.dit_attn_fwd_mx(*args, None, 0, None) == expect, why
 
 
 @pytest.mark.parametrize("args,expect,why", [
@@ -189,6 +191,43 @@ def test_mx_quantize_checks(lib, args, expect, why):
     if torch.cuda.is_available():
         pytest.skip("a GPU is present")
     assert lib.dit_attn_quantize_mx(*args, None) == expect, why
+
+
+WS = 0xB000000     # a fake workspace address, 16 MiB from the others
+
+
+@pytest.mark.parametrize("ws,nbytes,expect,why", [
+    (WS, 1 << 20, -3, "valid workspace (no GPU here: device error)"),
+    (None, 0, -3, "no workspace"),
+    (WS + 8, 0, -3, "a pointer without bytes is not used, so not checked"),
+    (None, 1 << 20, -1, "bytes without a pointer"),
+    (WS + 8, 1 << 20, -1, "workspace not 16-byte aligned"),
+    (WS, -16, -1, "negative size"),
+    (SA - 256, 1024, -1, "workspace runs into q"),
+    (SO + 512, 1 << 20, -1, "workspace inside o"),
+    (0x7000000 - 64, 128, -1, "workspace runs into lse"),
+])
+def test_workspace_checks(lib, ws, nbytes, expect, why):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    st = lib.dit_attn_fwd_strided(SA, SB, SC, SO, 2, 3, 8, 128, 0.125, 0, None, None, None, 0x7000000, ws, nbytes,
+                                  None)
+    assert st == expect, why
+
+
+def test_workspace_checks_of_the_list_and_scale_forms(lib):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    sparse = (SA, SB, SC, SO, 1, 2, 1000, 128, 0.1, 0, LB, LC, 16, None, None, None)
+    assert lib.dit_attn_fwd_blocksparse(*sparse, WS, 1 << 20, None) == -3
+    assert lib.dit_attn_fwd_blocksparse(*sparse, LB - 64, 1 << 20, None) == -1      # over the block lists
+    assert lib.dit_attn_fwd_blocksparse(*sparse, LC, 16, None) == -1                # over the counts
+    mx = (SA, SB, SC, QS, KS, VS, SO, 1, 2, 100, 128, 0.1, None)
+    assert lib.dit_attn_fwd_mx(*mx, WS, 1 << 20, None) == -3
+    assert lib.dit_attn_fwd_mx(*mx, VS - 16, 64, None) == -1                        # over the V scales
+    assert lib.dit_attn_fwd_mx(*mx, WS + 4, 64, None) == -1
 
 
 def test_fwd_ex_rejects_bad_lse(lib):

@@ -131,8 +131,9 @@ def test_full_lists_equal_dense(B, H, N):
     nq, nk = -(-N // 256), -(-N // 64)
     blocks = torch.arange(nk, dtype=torch.int32).expand(B, H, nq, nk).contiguous()
     counts = torch.full((B, H, nq), nk, dtype=torch.int32)
-    _, dense_plan = dit.dit_attn_plan(B, H, N, d, dit.DIT_ATTN_BF16, 0, 1, 0)
-    _, sparse_plan = dit.dit_attn_plan(B, H, N, d, dit.DIT_ATTN_BF16, nk, 1, 0)
+    # attention() passes the workspace the fastest schedule needs
+    _, dense_plan = dit.dit_attn_plan(B, H, N, d, dit.DIT_ATTN_BF16, 0, 1, 0, 1 << 40)
+    _, sparse_plan = dit.dit_attn_plan(B, H, N, d, dit.DIT_ATTN_BF16, nk, 1, 0, 1 << 40)
     say(f"[gpu] blocksparse full lists vs dense B={B} H={H} N={N} (schedules {dense_plan.schedule}, "
         f"{sparse_plan.schedule})")
     o, l = _sparse(q, k, v, blocks, counts, 1 / math.sqrt(d))

@@ -72,9 +72,9 @@ def test_streamk_strided_rows_bitwise_and_deterministic():
 def test_plan_for_the_current_device():
     import diffusion_transformer_attention_non_amd as dit
     n_cu = torch.cuda.get_device_properties(0).multi_processor_count
-    st, p = dit.dit_attn_plan(1, 3, 16896, 128, dit.DIT_ATTN_BF16, 0, 0, 0)
+    st, p = dit.dit_attn_plan(1, 3, 16896, 128, dit.DIT_ATTN_BF16, 0, 0, 0, 1 << 40)
     assert st == dit.DIT_ATTN_OK
-    st2, p2 = dit.dit_attn_plan(1, 3, 16896, 128, dit.DIT_ATTN_BF16, 0, 0, n_cu)
+    st2, p2 = dit.dit_attn_plan(1, 3, 16896, 128, dit.DIT_ATTN_BF16, 0, 0, n_cu, 1 << 40)
     assert st2 == dit.DIT_ATTN_OK
     assert (p.schedule, p.workgroups, p.workspace_bytes) == (p2.schedule, p2.workgroups, p2.workspace_bytes)
     say(f"[gpu] plan H=3 N=16896 on {n_cu} CUs: schedule {p.schedule}, {p.workgroups} workgroups")

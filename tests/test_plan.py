@@ -14,9 +14,16 @@ TILE, SPLIT, STREAMK = dit.DIT_ATTN_SCHED_TILE, dit.DIT_ATTN_SCHED_SPLIT, dit.DI
 ROW_BYTES = 129 * 4        # a partial row: 128 fp32 values and its log-sum-exp
 
 
-def plan(B, H, N, d=128, dtype=BF16, max_blocks=0, lse=False, n_cu=256):
-    st, p = dit.dit_attn_plan(B, H, N, d, dtype, max_blocks, lse, n_cu)
+BIG = 1 << 40              # a workspace larger than any plan needs: the fastest schedule
+MAX_WS = (1 << 17) * ROW_BYTES + (1 << 17) * 4    # the bound include/dit_attn.h states
+
+
+def plan(B, H, N, d=128, dtype=BF16, max_blocks=0, lse=False, n_cu=256, ws=BIG):
+    st, p = dit.dit_attn_plan(B, H, N, d, dtype, max_blocks, lse, n_cu, ws)
     assert st == dit.DIT_ATTN_OK, st
+    assert p.best_schedule == p.schedule or ws < p.workspace_wanted
+    if ws >= p.workspace_wanted:
+        assert p.workspace_bytes == p.workspace_wanted
     return p
 
 
@@ -89,7 +96,8 @@ def test_plan_invariants_over_shapes(n_cu):
         else:
             assert tiles <= 2 * n_cu
             min_range = max(4, -(-n_t // 13))
-            assert p.workgroups == min(n_cu, tiles * n_t // min_range) and p.workgroups >= 2
+            # one group per CU, at most 256 (2 x 256 slots of 256 partial rows: the workspace bound)
+            assert p.workgroups == min(n_cu, 256, tiles * n_t // min_range) and p.workgroups >= 2
             # the merge takes at most 16 parts of a cut tile: ranges are at least
             # ceil(n_t / 13) key tiles, so at most 14 boundaries fall inside a tile
             assert (tiles * n_t) // p.workgroups >= -(-n_t // 13)
@@ -103,7 +111,8 @@ def test_plan_rejects_bad_arguments():
            ((1, 1, 64, 128, 7, 0, 0, 256), dit.DIT_ATTN_EUNSUPPORTED),
            ((1, 1, 64, 128, BF16, 2, 0, 256), dit.DIT_ATTN_EINVAL),          # max_blocks past ceil(N/64)
            ((1, 1, 64, 64, BF16, 1, 0, 256), dit.DIT_ATTN_EUNSUPPORTED),     # sparse needs d = 128
-           ((1, 1, 64, 128, BF16, 0, 0, -1), dit.DIT_ATTN_EINVAL)]
+           ((1, 1, 64, 128, BF16, 0, 0, -1), dit.DIT_ATTN_EINVAL),
+           ((1, 1, 64, 128, BF16, 0, 0, 256, -1), dit.DIT_ATTN_EINVAL)]
     for args, want in bad:
         assert dit.dit_attn_plan(*args)[0] == want, args
 
@@ -140,3 +149,35 @@ def test_streamk_ranges_cover_each_pair_once_and_cut_tiles_into_at_most_16_parts
                     parts[t] += 1
             assert max(parts) <= 16, (B, H, N, n_cu, max(parts))
     assert seen >= 5
+
+
+def test_without_workspace_one_workgroup_per_tile_and_the_plan_says_what_one_buys():
+    """No workspace (dit_attn_fwd, dit_attn_fwd_ex, or a 0-byte one): one
+    workgroup per query tile, and the plan still reports the fastest schedule
+    and its workspace, so the fallback is never silent."""
+    for H, best in [(24, SPLIT), (3, STREAMK)]:
+        fast = plan(1, H, 16896)
+        p = plan(1, H, 16896, ws=0)
+        assert (p.schedule, p.workgroups, p.workspace_bytes) == (TILE, H * 66, 0)
+        assert p.best_schedule == best == fast.schedule
+        assert p.workspace_wanted == fast.workspace_bytes > 0
+        p = plan(1, H, 16896, ws=fast.workspace_bytes)      # exactly enough
+        assert p.schedule == best
+
+
+def test_a_workspace_too_small_is_an_error_not_a_fallback():
+    need = plan(1, 24, 16896).workspace_bytes
+    for ws in (16, need - 16):
+        st, _ = dit.dit_attn_plan(1, 24, 16896, 128, BF16, 0, 0, 256, ws)
+        assert st == dit.DIT_ATTN_EWORKSPACE
+    # a shape whose fastest schedule needs none takes any workspace
+    assert plan(1, 1, 256, ws=16).schedule == TILE
+
+
+@pytest.mark.parametrize("n_cu", [80, 256])
+def test_workspace_never_exceeds_the_stated_bound(n_cu):
+    worst = 0
+    for B, H, N in itertools.product([1, 2, 3], [1, 3, 6, 24, 48, 100], [300, 4608, 16896, 25088, 65536]):
+        for dtype, lse in [(BF16, False), (FP8, True)]:
+            worst = max(worst, plan(B, H, N, dtype=dtype, lse=lse, n_cu=n_cu).workspace_bytes)
+    assert 0 < worst <= MAX_WS
