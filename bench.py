@@ -342,8 +342,14 @@ def main(argv=None):
                          "traffic": None}}
 
     if not args.no_extras:
-        clocks_after = read_clocks()
-        line["clocks"] = {"before": clocks_before, "after": clocks_after}
+        # clocks under load: enqueue about a second of back-to-back calls, read
+        # the clocks from a child process while they run, then wait for them
+        n_load = max(10, int(1.0 / (wall / args.steps)))
+        for _ in range(n_load):
+            step()
+        during = [read_clocks() for _ in range(2)]
+        torch.cuda.synchronize()
+        line["clocks"] = {"idle_before": clocks_before, "under_load": during, "calls_enqueued": n_load}
 
         def step_short():
             st = dit.dit_attn_fwd(qd, kd, vd, od, B, H, N, d, scale, dit.DIT_ATTN_BF16, handle)

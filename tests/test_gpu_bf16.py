@@ -6,9 +6,9 @@ import pytest
 import torch
 
 import oracle
-from parity import check_bf16, check_lse, gpu_attention, say
+from parity import check_bf16, check_full, gpu_attention, oracle_workload, say
 from workloads import (WORKLOADS, coverage_pattern, constant_values, dominating_key, identical_keys,
-                       make_qkv, random_qkv, sample_rows)
+                       make_qkv, random_qkv)
 
 pytestmark = pytest.mark.gpu
 
@@ -16,10 +16,7 @@ pytestmark = pytest.mark.gpu
 def _full_check(q, k, v, scale, label, lse=True):
     say(f"[gpu] {label}: shape {tuple(q.shape)}")
     o, l = gpu_attention(q, k, v, scale, want_lse=lse)
-    o_ref, l_ref, a_ref = oracle.attention(q, k, v, scale, want_abs=True)
-    check_bf16(o, o_ref, a_ref, label)
-    if lse:
-        check_lse(l, l_ref, label)
+    check_full(o, l, q, k, scale, oracle.attention(q, k, v, scale, want_abs=True), label)
     return o
 
 
@@ -41,18 +38,21 @@ def test_batch_heads_and_peaked_small():
     _full_check(q * 4, k, v, 1 / math.sqrt(128), "B=2 H=3 N=777 peaked")
 
 
-@pytest.mark.parametrize("name,stride", [("t2i_1024", 16), ("t2i_2048", 64), ("t2i_2048_peaked", 64),
-                                         ("i2i_2048", 96), ("t2i_2048_h6", 32), ("t2i_2048_h3", 32)])
-def test_workload_sampled_rows(name, stride):
+@pytest.mark.timeout(900)
+# t2i_2048 last: its oracle result stays cached for the fp8 spec gate on the same tensors
+@pytest.mark.parametrize("name", ["t2i_1024", "t2i_2048_peaked", "i2i_2048", "t2i_2048_h6", "t2i_2048_h3",
+                                  "t2i_2048"])
+def test_workload_every_row(name):
+    """Every element of every workload at its full size, in the launch
+    configuration the benchmark times (the binding passes the workspace the
+    fastest schedule needs): split last round at 24 heads, stream-K at 3 and
+    6 heads, against the fp64 oracle on the same inputs."""
     w = WORKLOADS[name]
     q, k, v = make_qkv(w)
     scale = 1 / math.sqrt(w.d)
-    say(f"[gpu] {name}: B={w.B} H={w.H} N={w.N} d={w.d}")
+    say(f"[gpu] {name}: B={w.B} H={w.H} N={w.N} d={w.d}, every row")
     o, l = gpu_attention(q, k, v, scale, want_lse=True)
-    rows = sample_rows(w.N, seed=0, n_edge=128, stride=stride)
-    o_ref, l_ref, a_ref = oracle.attention(q, k, v, scale, rows=rows, want_abs=True)
-    check_bf16(o[:, :, rows], o_ref, a_ref, f"{name} ({rows.size} rows/head)")
-    check_lse(l[:, :, rows], l_ref, name)
+    check_full(o, l, q, k, scale, oracle_workload(name), f"{name} (all {w.N} rows/head)")
 
 
 # ------------------------------------------------------------ exact structure

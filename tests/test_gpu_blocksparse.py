@@ -13,7 +13,7 @@ import pytest
 import torch
 
 import oracle
-from parity import LSE_ATOL, LSE_RTOL, check_bf16, say
+from parity import check_bf16, lse_tolerance, logit_scale, say
 from workloads import make_qkv, random_kv_blocks, random_qkv, sample_rows
 
 pytestmark = pytest.mark.gpu
@@ -36,13 +36,13 @@ def _sparse(q, k, v, blocks, counts, scale, lse=True):
     return o, l
 
 
-def _check_lse(l_gpu, l_ref, label):
+def _check_lse(l_gpu, l_ref, tol, label):
     """As for dense rows; rows of empty lists must be -inf on both sides."""
     empty = np.isneginf(l_ref)
     assert np.array_equal(np.isneginf(l_gpu), empty), label
     err = np.abs(l_gpu[~empty] - l_ref[~empty])
     say(f"  {label} lse: max {float(err.max()) if err.size else 0.0:.3e}")
-    assert (err <= LSE_ATOL + LSE_RTOL * np.abs(l_ref[~empty])).all(), label
+    assert (err <= tol[~empty]).all(), label
 
 
 def _compare(q, k, v, blocks, counts, scale, label, rows=None):
@@ -55,7 +55,8 @@ def _compare(q, k, v, blocks, counts, scale, label, rows=None):
     empty = np.isneginf(l_ref)
     assert np.all(og[empty] == 0.0), label
     check_bf16(og, o_ref, a_ref, label)
-    _check_lse(lg, l_ref, label)
+    tol = lse_tolerance(q.shape[2], np.where(empty, 0.0, l_ref), logit_scale(q, k, scale, rows))
+    _check_lse(lg, l_ref, tol, label)
     return o, l
 
 

@@ -10,7 +10,7 @@ import pytest
 import torch
 
 import oracle
-from parity import check_bf16, check_lse, say
+from parity import check_full, say
 from workloads import WORKLOADS, make_qkv, random_qkv
 
 pytestmark = pytest.mark.gpu
@@ -67,9 +67,8 @@ def test_fused_qkv_against_oracle():
     scale = 1 / math.sqrt(128)
     qf, kf, vf = _fused_views(q, k, v, dev)
     o, l = _run(qf, kf, vf, scale)
-    o_ref, l_ref, a_ref = oracle.attention(q, k, v, scale, want_abs=True)
-    check_bf16(o.float().cpu().double().numpy(), o_ref, a_ref, "fused QKV (B=1 H=4 N=777)")
-    check_lse(l.cpu().double().numpy(), l_ref, "fused QKV")
+    check_full(o.float().cpu().double().numpy(), l.cpu().double().numpy(), q, k, scale,
+               oracle.attention(q, k, v, scale, want_abs=True), "fused QKV (B=1 H=4 N=777)")
 
 
 def test_fp8_bnhd_bitwise():

@@ -14,23 +14,21 @@ import pytest
 import torch
 
 import oracle
-from parity import check_bf16, check_lse, gpu_attention, say
+from parity import check_bf16, check_full, gpu_attention, say
 from workloads import coverage_pattern, random_qkv, sample_rows
 
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
 
 
+@pytest.mark.timeout(600)
 @pytest.mark.parametrize("B,H,N", [(1, 4, 12800), (1, 1, 16896), (1, 5, 16896), (1, 3, 16896)])
-def test_streamk_sampled_rows(B, H, N):
+def test_streamk_every_row(B, H, N):
     q, k, v = random_qkv(B, H, N, 128, seed=900 + H)
-    say(f"[gpu] stream-K B={B} H={H} N={N}")
+    say(f"[gpu] stream-K B={B} H={H} N={N}, every row")
     o, l = gpu_attention(q, k, v, 1 / math.sqrt(128), want_lse=True)
-    # every 256-row tile boundary region and a stride: cut tiles are all over
-    rows = sample_rows(N, seed=H, n_edge=256, stride=24)
-    o_ref, l_ref, a_ref = oracle.attention(q, k, v, 1 / math.sqrt(128), rows=rows, want_abs=True)
-    check_bf16(o[:, :, rows], o_ref, a_ref, f"stream-K H={H} N={N}")
-    check_lse(l[:, :, rows], l_ref, f"stream-K H={H} N={N}")
+    check_full(o, l, q, k, 1 / math.sqrt(128), oracle.attention(q, k, v, 1 / math.sqrt(128), want_abs=True),
+               f"stream-K H={H} N={N}")
 
 
 @pytest.mark.parametrize("H,N", [(3, 16896), (4, 12800), (1, 16896)])
