@@ -34,11 +34,19 @@
 // Softmax without a per-tile maximum. The running maximum m (log2 units, per
 // query row) starts at the exact maximum of the first 32 keys. bf16 keeps
 // 8 significant bits at any scale, so probabilities relative to a stale m lose
-// nothing as long as nothing overflows: m moves only when a lane's sum of a
+// nothing as long as nothing overflows: m moves only when a sum of 16 of a
 // sub-tile's probabilities exceeds 2^64 (or is not finite). That rare path
 // recomputes the sub-tile's logits from K (still in LDS), takes their exact
-// maximum, rescales O and l and recomputes P. The row sums are of the
-// unrounded probabilities, so the log-sum-exp is the exact one.
+// maximum, rescales O and l and recomputes P.
+//
+// Row sums. O is divided by the sum of the bf16-rounded probabilities that
+// the P V products multiply V with, so every output row is a convex
+// combination of rows of V; a row that one key dominates then keeps nothing
+// of that key's rounding error. The sums come from the matrix core: one
+// 16x16x32 product of each packed P^T fragment with a ones operand (no VALU
+// adds), which also feeds the overflow test. The EXACT_LSE form, used when a
+// log-sum-exp is requested, adds fp32 sums of the unrounded probabilities for
+// it, so the log-sum-exp is the exact one; O is the same in both forms.
 //
 // Schedules. pipe_tile runs one query tile over a range of key tiles.
 // attn_fwd_bf16_pipe_kernel gives each workgroup a whole tile, or one key
@@ -122,7 +130,7 @@ __device__ __forceinline__ void dma_b128(i32x4_t rsrc, int voffset, unsigned lds
 // a split tile's part `part` of split.parts takes its share of the list).
 // ws_index >= 0: write the rows normalised over this range, with their
 // log2-sum-exp, to workspace slot ws_index; otherwise write O (and the LSE).
-template <class C, bool SPARSE>
+template <class C, bool SPARSE, bool EXACT_LSE>
 __device__ __forceinline__ void pipe_tile(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
                                           const uint16_t* __restrict__ Vg, uint16_t* __restrict__ Og,
                                           float* __restrict__ LSEg, int N, int n_qtiles, float scale_log2,
@@ -181,6 +189,7 @@ __device__ __forceinline__ void pipe_tile(const uint16_t* __restrict__ Qg, const
 #pragma unroll
           for (int c = 0; c < D / 2; c += 4) *(f32x4_t*)(orow + c) = f32x4_t{0.f, 0.f, 0.f, 0.f};
           if (hh == 0) split.ws_lse[(size_t)ws_index * C::kBR + r] = -INFINITY;
+          if (EXACT_LSE && hh == 0) split.ws_lse_out[(size_t)ws_index * C::kBR + r] = -INFINITY;
         } else if (row < N) {
           uint16_t* orow = Og + obase + (long long)row * L.on + hh * (D / 2);
 #pragma unroll
@@ -299,15 +308,14 @@ __device__ __forceinline__ void pipe_tile(const uint16_t* __restrict__ Qg, const
     for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
     return pair_max(mx) * scale_log2;      // scale_log2 > 0
   };
-  // P = 2^t for 8 consecutive entries of t, packed to bf16
-  // p = 2^t[i], summed unrounded into ls; pack_word puts two p as bf16 word
-  // e & 3 of out[e >> 2]. (Row sums with v_dot2 on the packed P would
-  // wait for the matrix core each time: dot instructions issue behind the
-  // MFMA in flight.)
+  // p = 2^t[i] (EXACT_LSE: also summed unrounded into ls); pack_word puts
+  // two p as bf16 word e & 3 of out[e >> 2].
   auto exp_one = [&](const f32x16_t& t, int i, float& ls) __attribute__((always_inline)) {
     const float p = fast_exp2(t[i]);
-    ls += p;
-    asm volatile("" : "+v"(ls));       // keeps the add in this step
+    if constexpr (EXACT_LSE) {
+      ls += p;
+      asm volatile("" : "+v"(ls));     // keeps the add in this step
+    }
     return p;
   };
   // exp2 now, its row-sum add later: the add waits on the transcendental unit
@@ -324,13 +332,26 @@ __device__ __forceinline__ void pipe_tile(const uint16_t* __restrict__ Qg, const
     w[e & 3] = word;
     out[e >> 2] = __builtin_bit_cast(bf16x8_t, w);
   };
-  // the row-sum adds and the pack of two p, placed at this point
+  // the pack of two p (EXACT_LSE: and their unrounded adds), placed at this point
   auto sum_pack = [&](float& ls, float a, float b, int e, bf16x8_t (&out)[2]) __attribute__((always_inline)) {
     asm volatile("" : "+v"(a), "+v"(b));
-    ls += a;
-    ls += b;
-    asm volatile("" : "+v"(ls));
+    if constexpr (EXACT_LSE) {
+      ls += a;
+      ls += b;
+      asm volatile("" : "+v"(ls));
+    }
     pack_word(a, b, e, out);
+  };
+  // Row sums of the packed P on the matrix core. Read as the B operand of the
+  // 16x16x32 product, lane 16 g + c of a P^T fragment is column c, k-group g
+  // (query c + 16 (g & 1), 8 of the fragment's 16 keys); A holds ones exactly
+  // where row r meets k-group r, so output row r, column c sums the 8 values
+  // of lane 16 r + c. Lanes 0..15 receive the sums of queries c (rows 0, 2)
+  // and c + 16 (rows 1, 3); the other lanes' rows are zero.
+  const int one_w = (lane & 15) == (lane >> 4) ? 0x3F803F80 : 0;        // two bf16 1.0
+  const bf16x8_t ones = __builtin_bit_cast(bf16x8_t, i32x4_t{one_w, one_w, one_w, one_w});
+  auto psum = [&](const bf16x8_t& pt, const f32x4_t& c) __attribute__((always_inline)) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pt, c, 0, 0, 0);
   };
 
   f32x16_t acc[2][DB];
@@ -341,7 +362,9 @@ __device__ __forceinline__ void pipe_tile(const uint16_t* __restrict__ Qg, const
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[qb][db][r] = 0.f;
   float mc[2];                 // running row maxima, log2 units
-  float l_run[2] = {0.f, 0.f};
+  // row sums of the rounded P in lanes 0..15: query c of each block in l_lo,
+  // query c + 16 in l_hi; EXACT_LSE: this lane's sums of the unrounded p
+  float l_lo[2] = {0.f, 0.f}, l_hi[2] = {0.f, 0.f}, l_ex[2] = {0.f, 0.f};
   f32x16_t t0;                 // exponent arguments of the current sub-tile, query block 0
   f32x16_t s1;                 // raw logits of the current sub-tile, query block 1
   bf16x8_t pA[2][2], pB[2][2]; // P of two consecutive sub-tiles [query block][key half]
@@ -398,7 +421,9 @@ __device__ __forceinline__ void pipe_tile(const uint16_t* __restrict__ Qg, const
   auto sub = [&](int j, bf16x8_t (&pin)[2][2], bf16x8_t (&pout)[2][2], auto mask_c, auto&& dma)
       __attribute__((always_inline)) {
     constexpr bool MASK = decltype(mask_c)::value;
-    float ls0 = 0.f, ls1 = 0.f;
+    float ls0 = 0.f, ls1 = 0.f;   // EXACT_LSE only
+    const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
+    f32x4_t rs0, rs1;          // matrix-core sums of P_j, query blocks 0 and 1
     f32x16_t& t1 = s1;         // in place
     f32x16_t sa, sb;           // S_{j+1} of query blocks 0 and 1
     const char* vb = vbase(j);
@@ -420,6 +445,7 @@ __device__ __forceinline__ void pipe_tile(const uint16_t* __restrict__ Qg, const
           for (int r = 0; r < 16; ++r) sa[r] = 0.f;
         }
         sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[st], qf[0][st], sa, 0, 0, 0);
+        if (st == 4) rs0 = psum(pout[0][0], zero4);   // words 0-3 were packed in steps 0-3
         sum_pack(ls0, pa, pb, st, pout[0]);
         if (st & 1) read_vfrag(vb, 0, db);      // both query blocks have used vf[0][db]
         DIT_FENCE();
@@ -444,6 +470,8 @@ __device__ __forceinline__ void pipe_tile(const uint16_t* __restrict__ Qg, const
           for (int r = 0; r < 16; ++r) sb[r] = 0.f;
         }
         sb = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[st], qf[1][st], sb, 0, 0, 0);
+        if (st == 0) rs0 = psum(pout[0][1], rs0);
+        if (st == 4) rs1 = psum(pout[1][0], zero4);
         sum_pack(ls1, pa, pb, st, pout[1]);
         read_kfrag(kb2, st);                     // kf[st] is free: K_{j+2}
         if (st & 1) read_vfrag(vb, 1, db);
@@ -457,9 +485,14 @@ __device__ __forceinline__ void pipe_tile(const uint16_t* __restrict__ Qg, const
     // The packed P must exist here: without this the compiler sinks the bf16
     // packs past the rare-path branch, out of the MFMA phases.
     asm volatile("" ::"v"(pout[0][0]), "v"(pout[0][1]), "v"(pout[1][0]), "v"(pout[1][1]));
-    // ---- rare path: a row sum of sub-tile j passed 2^64 or is not finite
-    const bool bad = !(ls0 <= kPipeSumLimit) || !(ls1 <= kPipeSumLimit);
-    if (__builtin_expect(__builtin_amdgcn_ballot_w64(bad) != 0, 0)) {
+    rs1 = psum(pout[1][1], rs1);
+    // ---- rare path: a sum of 16 of sub-tile j's p passed 2^64 or is not
+    // finite. The sums are >= +0 or NaN, so their bit patterns order like the
+    // values, with every NaN above +inf: one unsigned maximum decides.
+    auto bits = [](float x) { return __float_as_uint(x); };
+    const uint32_t big = max(max(max(bits(rs0[0]), bits(rs0[1])), max(bits(rs0[2]), bits(rs0[3]))),
+                             max(max(bits(rs1[0]), bits(rs1[1])), max(bits(rs1[2]), bits(rs1[3]))));
+    if (__builtin_expect(__builtin_amdgcn_ballot_w64(big > __float_as_uint(kPipeSumLimit)) != 0, 0)) {
       read_kfrags(j);                      // K tiles j/2 and (j+2)/2 are still in their slots
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
@@ -470,7 +503,9 @@ __device__ __forceinline__ void pipe_tile(const uint16_t* __restrict__ Qg, const
         }
         const float m_new = fmaxf(mc[qb], row_max(s));
         const float alpha = fast_exp2(mc[qb] - m_new);
-        l_run[qb] *= alpha;
+        l_lo[qb] *= __shfl(alpha, lane & 15);
+        l_hi[qb] *= __shfl(alpha, (lane & 15) + 16);
+        if constexpr (EXACT_LSE) l_ex[qb] *= alpha;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -491,10 +526,18 @@ __device__ __forceinline__ void pipe_tile(const uint16_t* __restrict__ Qg, const
           pack_word(pa, exp_one(s, 2 * e + 1, ls), e, pout[qb]);
         }
       }
+      rs0 = psum(pout[0][1], psum(pout[0][0], zero4));
+      rs1 = psum(pout[1][1], psum(pout[1][0], zero4));
       read_kfrags(j + 2);
     }
-    l_run[0] += ls0;
-    l_run[1] += ls1;
+    l_lo[0] += rs0[0] + rs0[2];
+    l_hi[0] += rs0[1] + rs0[3];
+    l_lo[1] += rs1[0] + rs1[2];
+    l_hi[1] += rs1[1] + rs1[3];
+    if constexpr (EXACT_LSE) {
+      l_ex[0] += ls0;
+      l_ex[1] += ls1;
+    }
   };
 
   // One 64-key tile u. It streams in K tile u+3 (during its first
@@ -577,13 +620,20 @@ __device__ __forceinline__ void pipe_tile(const uint16_t* __restrict__ Qg, const
   // until every wave has read its last fragments. Each wave stages and reads
   // back only its own 64 rows; one wave's LDS operations complete in order, and
   // the waits keep the compiler from moving the reads above the writes.
+  // the rounded-P row sum of this lane's query, from lanes 0..15
+  float l_q[2];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const float lo = __shfl(l_lo[qb], l32 & 15), hi = __shfl(l_hi[qb], l32 & 15);
+    l_q[qb] = l32 < 16 ? lo : hi;
+  }
   __syncthreads();
   if (ws_index >= 0) {
     // one key range of a split tile: fp32 rows normalised over the range
     char* wst = smem + wave * (64 * C::kWsRow);
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-      const float l_tot = pair_sum(l_run[qb]);
+      const float l_tot = l_q[qb];
       const float inv = 1.0f / l_tot;
       char* srow = wst + (qb * 32 + l32) * C::kWsRow;
 #pragma unroll
@@ -595,7 +645,12 @@ __device__ __forceinline__ void pipe_tile(const uint16_t* __restrict__ Qg, const
                        acc[qb][db][i * 4 + 3] * inv};
           *(f32x4_t*)(srow + d0 * 4) = w;
         }
-      if (hh == 0) split.ws_lse[(size_t)ws_index * C::kBR + wave * 64 + qb * 32 + l32] = mc[qb] + __log2f(l_tot);
+      const size_t r = (size_t)ws_index * C::kBR + wave * 64 + qb * 32 + l32;
+      if (hh == 0) split.ws_lse[r] = mc[qb] + __log2f(l_tot);
+      if constexpr (EXACT_LSE) {
+        const float l_exact = pair_sum(l_ex[qb]);
+        if (hh == 0) split.ws_lse_out[r] = mc[qb] + __log2f(l_exact);
+      }
     }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     float* wrows = split.ws_o + ((size_t)ws_index * C::kBR + wave * 64) * D;
@@ -610,8 +665,7 @@ __device__ __forceinline__ void pipe_tile(const uint16_t* __restrict__ Qg, const
   char* ost = smem + wave * (64 * C::kORow);
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
-    const float l_tot = pair_sum(l_run[qb]);
-    const float inv = 1.0f / l_tot;
+    const float inv = 1.0f / l_q[qb];
     char* srow = ost + (qb * 32 + l32) * C::kORow;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
@@ -623,9 +677,11 @@ __device__ __forceinline__ void pipe_tile(const uint16_t* __restrict__ Qg, const
         w.y = pack_bf16x2(acc[qb][db][i * 4 + 2] * inv, acc[qb][db][i * 4 + 3] * inv);
         *(uint2*)(srow + d0 * 2) = w;
       }
-    const int row = q0 + qb * 32 + l32;
-    if (LSEg != nullptr && hh == 0 && row < N)
-      LSEg[(size_t)bh * N + row] = (mc[qb] + __log2f(l_tot)) * 0.6931471805599453f;
+    if constexpr (EXACT_LSE) {
+      const float l_exact = pair_sum(l_ex[qb]);
+      const int row = q0 + qb * 32 + l32;
+      if (hh == 0 && row < N) LSEg[(size_t)bh * N + row] = (mc[qb] + __log2f(l_exact)) * 0.6931471805599453f;
+    }
   }
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   const int chunk = lane & 15;
@@ -638,7 +694,8 @@ __device__ __forceinline__ void pipe_tile(const uint16_t* __restrict__ Qg, const
   }
 }
 
-template <class C, bool SPARSE = false>
+// EXACT_LSE: the form that writes a log-sum-exp (LSEg non-null).
+template <class C, bool SPARSE, bool EXACT_LSE>
 __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void attn_fwd_bf16_pipe_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
                                const uint16_t* __restrict__ Vg, uint16_t* __restrict__ Og,
@@ -659,7 +716,8 @@ void attn_fwd_bf16_pipe_kernel(const uint16_t* __restrict__ Qg, const uint16_t* 
     u1 = (part + 1) * n_t / split.parts;
     ws_index = part * split.n_split + ti;
   }
-  pipe_tile<C, SPARSE>(Qg, Kg, Vg, Og, LSEg, N, n_qtiles, scale_log2, split, L, kvb, tile, u0, u1, ws_index, part);
+  pipe_tile<C, SPARSE, EXACT_LSE>(Qg, Kg, Vg, Og, LSEg, N, n_qtiles, scale_log2, split, L, kvb, tile, u0, u1,
+                                  ws_index, part);
 }
 
 // Stream-K schedule: `groups` workgroups (one per CU) cut the tiles * n_t
@@ -671,12 +729,13 @@ void attn_fwd_bf16_pipe_kernel(const uint16_t* __restrict__ Qg, const uint16_t* 
 // range covers whole are written directly.
 struct StreamK {
   float* ws_o;     // [2 groups][256][128]
-  float* ws_lse;   // [2 groups][256], log2 units
+  float* ws_lse;   // [2 groups][256], log2 units: the merge weights of O (rounded-P sums)
+  float* ws_lse_out;  // NULL, or [2 groups][256]: the exact sums, for the LSE output
   int groups;
   int tiles;       // query tiles of the call
 };
 
-template <class C>
+template <class C, bool EXACT_LSE>
 __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void attn_fwd_bf16_streamk_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
                                   const uint16_t* __restrict__ Vg, uint16_t* __restrict__ Og,
@@ -687,14 +746,14 @@ void attn_fwd_bf16_streamk_kernel(const uint16_t* __restrict__ Qg, const uint16_
   // neighbouring groups (one XCD) share the tile cut between them: K/V reuse in L2
   const int g = xcd_remap(blockIdx.x, gridDim.x);
   const long long s = work * g / sk.groups, e = work * (g + 1) / sk.groups;
-  const PipeSplit ws{0, 0, 1, sk.ws_o, sk.ws_lse, nullptr};
+  const PipeSplit ws{0, 0, 1, sk.ws_o, sk.ws_lse, sk.ws_lse_out};
   for (long long pos = s; pos < e;) {
     const int tile = (int)(pos / n_t);
     const int u0 = (int)(pos - (long long)tile * n_t);
     const int u1 = (int)min((long long)n_t, (long long)u0 + (e - pos));
     const int slot = (u0 == 0 && u1 == n_t) ? -1 : (pos == s ? 2 * g : 2 * g + 1);
-    pipe_tile<C, false>(Qg, Kg, Vg, Og, LSEg, N, n_qtiles, scale_log2, ws, L, KvBlocks{nullptr, nullptr, 0}, tile,
-                        u0, u1, slot, 0);
+    pipe_tile<C, false, EXACT_LSE>(Qg, Kg, Vg, Og, LSEg, N, n_qtiles, scale_log2, ws, L,
+                                   KvBlocks{nullptr, nullptr, 0}, tile, u0, u1, slot, 0);
     __syncthreads();       // every wave is done with the LDS slots before the next tile's DMA
     pos += u1 - u0;
   }
@@ -755,7 +814,13 @@ __global__ __launch_bounds__(256) void attn_streamk_combine_kernel(uint16_t* __r
     out.x = pack_bf16x2(o[0] * inv, o[1] * inv);
     out.y = pack_bf16x2(o[2] * inv, o[3] * inv);
     *(uint2*)(Og + L.out_off(bh) + (long long)row * L.on + c) = out;
-    if (LSEg != nullptr && c == 0) LSEg[(size_t)bh * N + row] = (mx + __log2f(wsum)) * 0.6931471805599453f;
+    if (LSEg != nullptr && c == 0) {
+      // the exact sums of the parts (the merge weights above are the rounded-P sums)
+      float lmx = -INFINITY, lsum = 0.f;
+      for (int i = 0; i < n_parts; ++i) lmx = fmaxf(lmx, sk.ws_lse_out[(size_t)slots[i] * BR + r]);
+      for (int i = 0; i < n_parts; ++i) lsum += fast_exp2(sk.ws_lse_out[(size_t)slots[i] * BR + r] - lmx);
+      LSEg[(size_t)bh * N + row] = (lmx + __log2f(lsum)) * 0.6931471805599453f;
+    }
   }
 }
 

@@ -39,14 +39,17 @@ hipError_t allow_lds_bf16() {
 }
 template <class C>
 hipError_t allow_lds_pipe() {
-  const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_fwd_bf16_pipe_kernel<C, false>),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, C::kLdsBytes);
-  if (e != hipSuccess) return e;
-  const hipError_t e2 = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_fwd_bf16_pipe_kernel<C, true>),
-                                            hipFuncAttributeMaxDynamicSharedMemorySize, C::kLdsBytes);
-  if (e2 != hipSuccess) return e2;
-  return hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_fwd_bf16_streamk_kernel<C>),
-                             hipFuncAttributeMaxDynamicSharedMemorySize, C::kLdsBytes);
+  const void* kernels[6] = {reinterpret_cast<const void*>(&attn_fwd_bf16_pipe_kernel<C, false, false>),
+                            reinterpret_cast<const void*>(&attn_fwd_bf16_pipe_kernel<C, false, true>),
+                            reinterpret_cast<const void*>(&attn_fwd_bf16_pipe_kernel<C, true, false>),
+                            reinterpret_cast<const void*>(&attn_fwd_bf16_pipe_kernel<C, true, true>),
+                            reinterpret_cast<const void*>(&attn_fwd_bf16_streamk_kernel<C, false>),
+                            reinterpret_cast<const void*>(&attn_fwd_bf16_streamk_kernel<C, true>)};
+  for (const void* k : kernels) {
+    const hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, C::kLdsBytes);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 template <class C>
 hipError_t allow_lds_fp8() {
@@ -238,7 +241,8 @@ int make_plan(int kind, long long BH, int N, int n_cu, int max_blocks, bool lse,
       p->groups = groups;
       p->workgroups = groups;
       p->units = (size_t)2 * groups * kBR;
-      p->ws_floats = p->units * (kD + 1);
+      // with an LSE output, exact sums of their own besides the rounded-P merge weights
+      p->ws_floats = p->units * (kD + 1) + (lse ? p->units : 0);
       return DIT_ATTN_OK;
     }
   }
@@ -248,9 +252,9 @@ int make_plan(int kind, long long BH, int N, int n_cu, int max_blocks, bool lse,
     p->schedule = DIT_ATTN_SCHED_SPLIT;
     p->workgroups = (long long)p->sp.n_full + (long long)p->sp.n_split * p->sp.parts;
     p->units = (size_t)p->sp.n_split * p->sp.parts * kBR;
-    // fp8 with an LSE output: O's merge weights come from the e4m3 sums, the
-    // LSE from exact sums of its own
-    p->ws_floats = p->units * (kD + 1) + (kind == kPlanFp8D128 && lse ? p->units : 0);
+    // with an LSE output: O's merge weights come from the sums of the rounded
+    // P (bf16 or e4m3), the LSE from exact sums of its own
+    p->ws_floats = p->units * (kD + 1) + (lse ? p->units : 0);
   }
   return DIT_ATTN_OK;
 }
@@ -284,8 +288,10 @@ template <class C>
 int launch_streamk(const void* q, const void* k, const void* v, void* o, float* lse, int tiles, int N,
                    int n_qtiles, float scale_log2, hipStream_t st, int groups, const Layout& L, void* ws) {
   const size_t units = (size_t)2 * groups * C::kBR;
-  StreamK sk{static_cast<float*>(ws), static_cast<float*>(ws) + units * C::kD, groups, tiles};
-  hipLaunchKernelGGL(attn_fwd_bf16_streamk_kernel<C>, dim3((unsigned)groups), dim3(C::kThreads), C::kLdsBytes, st,
+  float* wsf = static_cast<float*>(ws);
+  StreamK sk{wsf, wsf + units * C::kD, lse != nullptr ? wsf + units * (C::kD + 1) : nullptr, groups, tiles};
+  auto* kernel = lse != nullptr ? &attn_fwd_bf16_streamk_kernel<C, true> : &attn_fwd_bf16_streamk_kernel<C, false>;
+  hipLaunchKernelGGL(kernel, dim3((unsigned)groups), dim3(C::kThreads), C::kLdsBytes, st,
                      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                      static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), lse, N, n_qtiles, scale_log2, sk,
                      L);
@@ -315,9 +321,10 @@ int launch_pipe(const void* q, const void* k, const void* v, void* o, float* lse
   if (plan.schedule == DIT_ATTN_SCHED_SPLIT) {
     sp.ws_o = static_cast<float*>(ws);
     sp.ws_lse = sp.ws_o + plan.units * C::kD;
+    sp.ws_lse_out = lse != nullptr ? sp.ws_lse + plan.units : nullptr;
   }
   const long long grid = (long long)sp.n_full + (long long)sp.n_split * sp.parts;
-  auto* kernel = &attn_fwd_bf16_pipe_kernel<C, SPARSE>;
+  auto* kernel = lse != nullptr ? &attn_fwd_bf16_pipe_kernel<C, SPARSE, true> : &attn_fwd_bf16_pipe_kernel<C, SPARSE, false>;
   hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(C::kThreads), C::kLdsBytes, st,
                      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                      static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), lse, N, n_qtiles,

@@ -78,6 +78,7 @@ def test_fwd_rejects_bad_arguments_strided_too(lib):
         assert lib.dit_attn_fwd_strided(*args, None, None, None, None, None, 0, None) == expect
 
 
+
 # (B, H, N, d) = (2, 3, 8, 64) bf16 at disjoint fake addresses 16 MiB apart
 SA, SB, SC, SO = 0x1000000, 0x2000000, 0x3000000, 0x4000000
 BNHD = (8 * 3 * 64, 64, 3 * 64)              # [B][N][H][d]
