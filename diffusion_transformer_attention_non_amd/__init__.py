@@ -12,7 +12,7 @@ import math
 
 from . import _lib
 from ._lib import (DIT_ATTN_BF16, DIT_ATTN_EDEVICE, DIT_ATTN_EINVAL, DIT_ATTN_ELAUNCH, DIT_ATTN_FP8_E4M3,
-                   DIT_ATTN_EWORKSPACE,
+                   DIT_ATTN_EWORKSPACE, DIT_ATTN_NOALLOC_SCRATCH_BYTES, dit_attn_fwd_noalloc,
                    DIT_ATTN_MX_ALONG_D, DIT_ATTN_MX_ALONG_TOKENS, DIT_ATTN_OK, DIT_ATTN_SPARSE_KV_BLOCK,
                    DIT_ATTN_SPARSE_Q_BLOCK, DIT_ATTN_EUNSUPPORTED, dit_attn_fwd, dit_attn_fwd_blocksparse,
                    dit_attn_fwd_ex, dit_attn_fwd_mx, dit_attn_fwd_strided, dit_attn_plan, dit_attn_quantize_e4m3,
@@ -27,7 +27,7 @@ __all__ = [
     "DIT_ATTN_SCHED_SPLIT", "DIT_ATTN_SCHED_STREAMK",
     "dit_attn_strerror", "dit_attn_version", "DIT_ATTN_BF16", "DIT_ATTN_FP8_E4M3", "DIT_ATTN_OK",
     "DIT_ATTN_EINVAL", "DIT_ATTN_EUNSUPPORTED", "DIT_ATTN_EDEVICE", "DIT_ATTN_ELAUNCH", "DIT_ATTN_EWORKSPACE",
-    "workspace_bytes",
+    "workspace_bytes", "dit_attn_fwd_noalloc", "DIT_ATTN_NOALLOC_SCRATCH_BYTES",
 ]
 
 

@@ -29,7 +29,10 @@ DIT_ATTN_SCHED_TILE = 0
 DIT_ATTN_SCHED_SPLIT = 1
 DIT_ATTN_SCHED_STREAMK = 2
 
-EXPORTED = ("dit_attn_fwd", "dit_attn_fwd_blocksparse", "dit_attn_fwd_ex", "dit_attn_fwd_mx", "dit_attn_fwd_strided",
+DIT_ATTN_NOALLOC_SCRATCH_BYTES = 68157440
+
+EXPORTED = ("dit_attn_fwd", "dit_attn_fwd_blocksparse", "dit_attn_fwd_ex", "dit_attn_fwd_mx", "dit_attn_fwd_noalloc",
+            "dit_attn_fwd_strided",
             "dit_attn_plan", "dit_attn_quantize_e4m3", "dit_attn_quantize_mx", "dit_attn_strerror",
             "dit_attn_version")
 
@@ -54,6 +57,8 @@ _lib.dit_attn_fwd_ex.restype = _i
 _lib.dit_attn_fwd_strided.argtypes = [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _vp, _vp, _vp, _vp, _vp, _i64,
                                       _vp]
 _lib.dit_attn_fwd_strided.restype = _i
+_lib.dit_attn_fwd_noalloc.argtypes = [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _vp, _vp, _vp, _vp, _vp]
+_lib.dit_attn_fwd_noalloc.restype = _i
 _lib.dit_attn_fwd_blocksparse.argtypes = [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _vp, _vp, _i,
                                           _vp, _vp, _vp, _vp, _i64, _vp]
 _lib.dit_attn_fwd_blocksparse.restype = _i
@@ -104,6 +109,14 @@ def dit_attn_fwd_strided(q, k, v, o, B, H, N, d, scale, dtype, qkv_strides=None,
     return _lib.dit_attn_fwd_strided(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, H, N, d, scale, dtype, qp, op,
                                      _ptr(descale_qkv), _ptr(lse), _ptr(workspace), int(workspace_bytes),
                                      _ptr(stream))
+
+
+def dit_attn_fwd_noalloc(q, k, v, o, B, H, N, d, scale, dtype, qkv_strides=None, o_strides=None,
+                         descale_qkv=None, lse=None, stream=None) -> int:
+    qs, qp = _strides3(qkv_strides)
+    os_, op = _strides3(o_strides)
+    return _lib.dit_attn_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, H, N, d, scale, dtype, qp, op,
+                                     _ptr(descale_qkv), _ptr(lse), _ptr(stream))
 
 
 def dit_attn_fwd_blocksparse(q, k, v, o, B, H, N, d, scale, dtype, kv_blocks, kv_counts, max_blocks,

@@ -427,6 +427,33 @@ int check_workspace(const void* ws, int64_t ws_bytes, const void* const* bufs, c
   return DIT_ATTN_OK;
 }
 
+// The library's own scratch for dit_attn_fwd_noalloc: every plan's partial
+// rows fit (kMaxSplitRows rows of kD + 1 floats, plus kMaxSplitRows floats of
+// exact LSE sums for fp8). Each GPU the library runs on holds one copy until
+// the process ends. Host code never uses the array's name as an address: the
+// kernels get the device address hipGetSymbolAddress returns for the current
+// device, looked up once per device on the entry point's first call there.
+constexpr size_t kScratchBytes = (size_t)kMaxSplitRows * (PipeCfg::kD + 1) * sizeof(float) +
+                                 (size_t)kMaxSplitRows * sizeof(float);   // 65 MiB
+static_assert(kScratchBytes == DIT_ATTN_NOALLOC_SCRATCH_BYTES, "the header states the scratch size");
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+
+// Device address of the current device's scratch array, or nullptr.
+void* scratch_address() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  void* ptr = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (ptr != nullptr) return ptr;
+  if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  g_scratch_ptr[dev].store(ptr, std::memory_order_release);
+  return ptr;
+}
+
 int plan_kind(int d, int dtype, int max_blocks) {
   return dtype == DIT_ATTN_FP8_E4M3 ? kPlanFp8D128
          : d == 64                  ? kPlanBf16D64
@@ -474,6 +501,33 @@ int dit_attn_fwd_strided(const void* q, const void* k, const void* v, void* o, i
     return launch_bf16<CfgBf16D64>(q, k, v, o, lse, c.bh, N, scale, st, c.L);
   }
   return launch_fp8<CfgFp8D128>(q, k, v, o, lse, descale_qkv, c.bh, N, scale, st, plan, workspace, c.L);
+}
+
+int dit_attn_fwd_noalloc(const void* q, const void* k, const void* v, void* o, int B, int H, int N, int d,
+                         float scale, int dtype, const int64_t* qkv_strides, const int64_t* o_strides,
+                         const float* descale_qkv, float* lse, void* stream) {
+  Checked c;
+  const int status = check_call(q, k, v, o, B, H, N, d, scale, dtype, qkv_strides, o_strides, descale_qkv, lse, &c);
+  if (status != DIT_ATTN_OK) return status;
+  const int dev_status = check_device();
+  if (dev_status != DIT_ATTN_OK) return dev_status;
+  Plan plan;
+  // the scratch array stands in for a workspace of its size: a plan that needs
+  // more is refused (DIT_ATTN_EWORKSPACE), never run on a smaller schedule
+  const int pst = resolve_plan(plan_kind(d, dtype, 0), c.bh, N, cu_count(), 0, lse != nullptr,
+                               (int64_t)kScratchBytes, &plan);
+  if (pst != DIT_ATTN_OK) return pst;
+  void* ws = nullptr;
+  if (plan.ws_floats > 0) {
+    ws = scratch_address();
+    if (ws == nullptr) return DIT_ATTN_EDEVICE;
+  }
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (dtype == DIT_ATTN_BF16) {
+    if (d == 128) return launch_pipe<CfgBf16D128>(q, k, v, o, lse, c.bh, N, scale, st, plan, ws, c.L);
+    return launch_bf16<CfgBf16D64>(q, k, v, o, lse, c.bh, N, scale, st, c.L);
+  }
+  return launch_fp8<CfgFp8D128>(q, k, v, o, lse, descale_qkv, c.bh, N, scale, st, plan, ws, c.L);
 }
 
 int dit_attn_fwd_blocksparse(const void* q, const void* k, const void* v, void* o, int B, int H, int N, int d,

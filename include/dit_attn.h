@@ -149,6 +149,30 @@ DIT_ATTN_API int dit_attn_fwd_strided(const void* q, const void* k, const void* 
                          const float* descale_qkv, float* lse,
                          void* workspace, int64_t workspace_bytes, void* stream);
 
+/*
+ * dit_attn_fwd_noalloc - dit_attn_fwd_strided without a workspace argument,
+ * for callers that cannot allocate (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation) but want the schedules a
+ * workspace buys. The split rows live in the library's own static device
+ * array of DIT_ATTN_NOALLOC_SCRATCH_BYTES (65 MiB; each GPU the library runs
+ * on holds one copy until the process ends), found with hipGetSymbolAddress
+ * on the first call on each device. The call allocates nothing.
+ *
+ * Every call on one GPU shares that GPU's array: calls that overlap in time
+ * on one GPU (other streams, other host threads) race and give undefined
+ * results; serialise them (one stream, or events). Nothing in the array needs
+ * to start at zero, and its contents after a call are undefined.
+ * A plan that needs more than the array holds returns DIT_ATTN_EWORKSPACE
+ * (no shape does on a device of at most 256 CUs). Arguments and other
+ * statuses as for dit_attn_fwd_strided; DIT_ATTN_EDEVICE also if the array's
+ * address cannot be had.
+ */
+#define DIT_ATTN_NOALLOC_SCRATCH_BYTES 68157440
+DIT_ATTN_API int dit_attn_fwd_noalloc(const void* q, const void* k, const void* v, void* o,
+                         int B, int H, int N, int d, float scale, int dtype,
+                         const int64_t* qkv_strides, const int64_t* o_strides,
+                         const float* descale_qkv, float* lse, void* stream);
+
 /* Tile sizes of dit_attn_fwd_blocksparse: query rows per list, keys per listed block. */
 #define DIT_ATTN_SPARSE_Q_BLOCK 256
 #define DIT_ATTN_SPARSE_KV_BLOCK 64

@@ -24,7 +24,7 @@ def lib():
 
 def test_header_declares_the_entry_points():
     assert _declared() == sorted(["dit_attn_fwd", "dit_attn_fwd_blocksparse", "dit_attn_fwd_ex", "dit_attn_fwd_mx",
-                                  "dit_attn_fwd_strided", "dit_attn_plan", "dit_attn_quantize_e4m3",
+                                  "dit_attn_fwd_noalloc", "dit_attn_fwd_strided", "dit_attn_plan", "dit_attn_quantize_e4m3",
                                   "dit_attn_quantize_mx", "dit_attn_strerror", "dit_attn_version"])
 
 
@@ -76,7 +76,20 @@ def test_fwd_rejects_bad_arguments_before_launch(lib, args, expect):
 def test_fwd_rejects_bad_arguments_strided_too(lib):
     for args, expect in [((0, B_, C, O, 1, 1, 8, 64, 0.125, 0), -1), ((A, B_, C, O, 1, 1, 8, 96, 0.125, 0), -2)]:
         assert lib.dit_attn_fwd_strided(*args, None, None, None, None, None, 0, None) == expect
+        assert lib.dit_attn_fwd_noalloc(*args, None, None, None, None, None) == expect
 
+
+def test_noalloc_scratch_size_is_the_stated_bound():
+    """The static scratch holds the largest workspace any plan asks for (2^17
+    partial rows of 129 floats plus 2^17 floats)."""
+    assert lib_scratch() == (1 << 17) * 129 * 4 + (1 << 17) * 4
+    text = open(HEADER).read()
+    assert f"#define DIT_ATTN_NOALLOC_SCRATCH_BYTES {lib_scratch()}" in text
+
+
+def lib_scratch():
+    import diffusion_transformer_attention_non_amd as pkg
+    return pkg.DIT_ATTN_NOALLOC_SCRATCH_BYTES
 
 
 # (B, H, N, d) = (2, 3, 8, 64) bf16 at disjoint fake addresses 16 MiB apart
