@@ -342,14 +342,29 @@ def main(argv=None):
                          "traffic": None}}
 
     if not args.no_extras:
-        # clocks under load: enqueue about a second of back-to-back calls, read
-        # the clocks from a child process while they run, then wait for them
-        n_load = max(10, int(1.0 / (wall / args.steps)))
+        # clocks under load: a thread reads them from a child process while
+        # about four seconds of back-to-back calls run; a reading taken after
+        # the queue drained (the stream already idle) is marked as such
+        import threading
+        n_load = max(10, int(4.0 / (wall / args.steps)))
+        during, done = [], threading.Event()
+
+        def sample():
+            time.sleep(0.5)
+            while not done.is_set() and len(during) < 4:
+                rec = read_clocks()
+                rec["busy"] = not done.is_set()
+                during.append(rec)
+
+        th = threading.Thread(target=sample)
+        th.start()
         for _ in range(n_load):
             step()
-        during = [read_clocks() for _ in range(2)]
         torch.cuda.synchronize()
-        line["clocks"] = {"idle_before": clocks_before, "under_load": during, "calls_enqueued": n_load}
+        done.set()
+        th.join()
+        line["clocks"] = {"idle_before": clocks_before, "under_load": [r for r in during if r["busy"]],
+                          "calls_enqueued": n_load}
 
         def step_short():
             st = dit.dit_attn_fwd(qd, kd, vd, od, B, H, N, d, scale, dit.DIT_ATTN_BF16, handle)

@@ -227,22 +227,32 @@ __device__ __forceinline__ void pipe_tile(const uint16_t* __restrict__ Qg, const
     kdo[m] = kc < D / 8 ? kr * rowb + kc * 16 : 64 * rowb;
     vdo[m] = vc < D / 8 ? vr * rowb + vc * 16 : 64 * rowb;
   }
+  // buffer descriptor of `rows` rows from address a: the range check
+  // zero-fills rows past them. Only descriptors of tiles that exist are used
+  // (rows >= 1); others are built but never read. Every field must come from
+  // the scalar unit: a VALU write of an SGPR (v_readfirstlane of a VALU
+  // result, a VALU min/max/med3) needs 5 wait states before a vector-memory
+  // instruction reads that SGPR, and the compiler does not insert them for
+  // the inline-asm DMA (the build refuses ISA with such a hazard). A plain
+  // min keeps it on the scalar unit, with its SCC use known to the compiler.
+  auto make_rsrc = [&](unsigned long long a, int rows) __attribute__((always_inline)) {
+    i32x4_t rs;
+    rs[0] = __builtin_amdgcn_readfirstlane((int)(unsigned)a);
+    rs[1] = __builtin_amdgcn_readfirstlane((int)((a >> 32) & 0xffffu));   // stride 0
+    rs[2] = __builtin_amdgcn_readfirstlane(min(64, rows) * rowb);          // bytes in range
+    rs[3] = 0x00020000;
+    return rs;
+  };
   // buffer descriptor of one 64-key tile: the range check zero-fills rows past N
   auto tile_rsrc = [&](const char* head, int t) __attribute__((always_inline)) {
-    int rows = min(64, N - t * 64);
+    int rows = N - t * 64;
     if constexpr (SPARSE) {
       // a listed index outside [0, n_t) (a malformed list) reads zeros
       const bool inside = t >= 0 && t < n_t;
       rows = inside ? rows : 0;
       t = inside ? t : 0;
     }
-    const unsigned long long a = (unsigned long long)(head + (long long)t * 64 * rowb);
-    i32x4_t rs;
-    rs[0] = __builtin_amdgcn_readfirstlane((int)(unsigned)a);
-    rs[1] = __builtin_amdgcn_readfirstlane((int)((a >> 32) & 0xffffu));   // stride 0
-    rs[2] = __builtin_amdgcn_readfirstlane(rows * rowb);                    // bytes in range
-    rs[3] = 0x00020000;
-    return rs;
+    return make_rsrc((unsigned long long)(head + (long long)t * 64 * rowb), rows);
   };
   // the m-th DMA instruction of this wave for one tile (instruction wave + 4 m)
   auto dma_one = [&](const i32x4_t& rs, const char* slot, const int (&off)[C::kDmaPerWave], int m)
@@ -273,11 +283,11 @@ __device__ __forceinline__ void pipe_tile(const uint16_t* __restrict__ Qg, const
   auto read_kfrag = [&](const char* kb, int ks) __attribute__((always_inline)) {
     kf[ks] = __builtin_bit_cast(bf16x8_t, *(const i32x4_t*)(kb + ks * 32));
   };
-  auto read_kfrags = [&](int j) {
-    const char* kb = kbase(j);
+  auto read_kfrags_at = [&](const char* kb) __attribute__((always_inline)) {
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) read_kfrag(kb, ks);
   };
+  auto read_kfrags = [&](int j) { read_kfrags_at(kbase(j)); };
   bf16x8_t vf[2][DB];
   auto vbase = [&](int j) { return vslot(j >> 1) + (j & 1) * 32 * VROW + v_rd; };
   auto read_vfrag = [&](const char* vb, int half, int db) __attribute__((always_inline)) {
@@ -368,6 +378,13 @@ __device__ __forceinline__ void pipe_tile(const uint16_t* __restrict__ Qg, const
   f32x16_t t0;                 // exponent arguments of the current sub-tile, query block 0
   f32x16_t s1;                 // raw logits of the current sub-tile, query block 1
   bf16x8_t pA[2][2], pB[2][2]; // P of two consecutive sub-tiles [query block][key half]
+  // LDS byte offsets of the ring slots the iteration of pipeline position u
+  // uses: K of positions u, u+1, u+3 and V of u, u+2. They rotate by one
+  // slot per iteration (scalar adds instead of a modulo per use).
+  struct Ring {
+    int k0, k1, k3, v0, v2;
+  };
+  Ring ring;
 
   // ---- prologue: K tiles u0..u0+2, V tiles u0, u0+1; the first sub-tile's
   // logits and their exact row maxima. The first iteration reads K u0, K u0+1
@@ -426,8 +443,8 @@ __device__ __forceinline__ void pipe_tile(const uint16_t* __restrict__ Qg, const
     f32x4_t rs0, rs1;          // matrix-core sums of P_j, query blocks 0 and 1
     f32x16_t& t1 = s1;         // in place
     f32x16_t sa, sb;           // S_{j+1} of query blocks 0 and 1
-    const char* vb = vbase(j);
-    const char* kb2 = kbase(j + 2);
+    const char* vb = smem + ring.v0 + (j & 1) * 32 * VROW + v_rd;      // V of position j / 2
+    const char* kb2 = smem + ring.k1 + (j & 1) * 32 * KROW + k_rd;     // K of sub-tile j + 2
     // ================= phase X: P_{j-1} V_{j-1} (keys 0-15), S_{j+1} block 0, P_j block 0
     {
       const float m1 = mc[1];
@@ -493,7 +510,7 @@ __device__ __forceinline__ void pipe_tile(const uint16_t* __restrict__ Qg, const
     const uint32_t big = max(max(max(bits(rs0[0]), bits(rs0[1])), max(bits(rs0[2]), bits(rs0[3]))),
                              max(max(bits(rs1[0]), bits(rs1[1])), max(bits(rs1[2]), bits(rs1[3]))));
     if (__builtin_expect(__builtin_amdgcn_ballot_w64(big > __float_as_uint(kPipeSumLimit)) != 0, 0)) {
-      read_kfrags(j);                      // K tiles j/2 and (j+2)/2 are still in their slots
+      read_kfrags_at(smem + ring.k0 + (j & 1) * 32 * KROW + k_rd);   // K tiles j/2 and (j+2)/2 are still in their slots
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
         f32x16_t s;
@@ -528,7 +545,7 @@ __device__ __forceinline__ void pipe_tile(const uint16_t* __restrict__ Qg, const
       }
       rs0 = psum(pout[0][1], psum(pout[0][0], zero4));
       rs1 = psum(pout[1][1], psum(pout[1][0], zero4));
-      read_kfrags(j + 2);
+      read_kfrags_at(kb2);
     }
     l_lo[0] += rs0[0] + rs0[2];
     l_hi[0] += rs0[1] + rs0[3];
@@ -540,6 +557,22 @@ __device__ __forceinline__ void pipe_tile(const uint16_t* __restrict__ Qg, const
     }
   };
 
+  {
+    auto rfl = [](int x) { return __builtin_amdgcn_readfirstlane(x); };
+    ring.k0 = rfl((u0 % C::kKSlots) * C::kSlot);
+    ring.k1 = rfl(((u0 + 1) % C::kKSlots) * C::kSlot);
+    ring.k3 = rfl(((u0 + 3) % C::kKSlots) * C::kSlot);
+    ring.v0 = rfl(C::kVBase + (u0 % C::kVSlots) * C::kSlot);
+    ring.v2 = rfl(C::kVBase + ((u0 + 2) % C::kVSlots) * C::kSlot);
+  }
+  auto advance_ring = [&]() __attribute__((always_inline)) {
+    ring.k3 = ring.k0;
+    ring.k0 = ring.k1;
+    ring.k1 = ring.k1 == (C::kKSlots - 1) * C::kSlot ? 0 : ring.k1 + C::kSlot;
+    ring.v2 = ring.v0;
+    ring.v0 = ring.v0 == C::kVBase + (C::kVSlots - 1) * C::kSlot ? C::kVBase : ring.v0 + C::kSlot;
+  };
+
   // One 64-key tile u. It streams in K tile u+3 (during its first
   // sub-iteration) and V tile u+2 (during its second), one DMA instruction on
   // every other phase-X step, and then waits for the tiles issued one iteration earlier
@@ -547,14 +580,16 @@ __device__ __forceinline__ void pipe_tile(const uint16_t* __restrict__ Qg, const
   // state (TAIL false) both DMAs exist and no key of tiles u, u+1 lies past N,
   // so the body has no branch but the rare path: a branch would let the
   // compiler sink the softmax work out of the MFMA phases.
-  // tk, tv: the key tiles at positions u + 3 (K) and u + 2 (V); before_wait()
-  // runs after the compute, ahead of the wait for the tiles.
-  auto iteration = [&](int u, auto tail_c, int tk, int tv, auto&& before_wait) __attribute__((always_inline)) {
+  // rk, rv: the descriptors of the key tiles at positions u + 3 (K) and u + 2
+  // (V); before_wait() runs after the compute, ahead of the wait for the
+  // tiles (the next iteration's scalar bookkeeping goes there, behind the
+  // last MFMAs in flight).
+  auto iteration = [&](int u, auto tail_c, const i32x4_t& rk, const i32x4_t& rv, auto&& before_wait)
+      __attribute__((always_inline)) {
     constexpr bool TAIL = decltype(tail_c)::value;
     const bool k_next = !TAIL || u + 3 < u1, v_next = !TAIL || u + 2 < u1;
-    const i32x4_t rk = tile_rsrc(Kh, tk), rv = tile_rsrc(Vh, tv);
-    const char* sk = kslot(u + 3);
-    const char* sv = vslot(u + 2);
+    const char* sk = smem + ring.k3;
+    const char* sv = smem + ring.v2;
     DIT_FENCE();
     // hook steps st = 0..3 issue instructions m = st, and m = 4 at st = 0
     static_assert(C::kDmaPerWave == 5, "DMA hook spreads 5 instructions over 4 steps");
@@ -572,6 +607,7 @@ __device__ __forceinline__ void pipe_tile(const uint16_t* __restrict__ Qg, const
     });
     DIT_FENCE();
     before_wait();
+    advance_ring();
     if (TAIL)
       __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     else
@@ -582,7 +618,6 @@ __device__ __forceinline__ void pipe_tile(const uint16_t* __restrict__ Qg, const
   // Sub-tiles past u1 that the pipeline touches (S of sub-tile 2 u1) read a
   // slot that is stale or zero: their values are never used.
   int u = u0;
-  auto nothing = [] {};
   if constexpr (SPARSE) {
     // A steady-state iteration loads the next one's K tile index while it
     // waits for its DMAs (a scalar load waited for at the top of the loop
@@ -590,17 +625,29 @@ __device__ __forceinline__ void pipe_tile(const uint16_t* __restrict__ Qg, const
     int tk = ktile(u0 + 3), tv = ktile(u0 + 2);
     for (; u + 3 < u1; ++u) {
       int tk_next;
-      iteration(u, flag_t<false>{}, tk, tv, [&] {
+      iteration(u, flag_t<false>{}, tile_rsrc(Kh, tk), tile_rsrc(Vh, tv), [&] {
         tk_next = ktile(u + 4);
         asm volatile("" : "+s"(tk_next));
       });
       tv = tk;
       tk = tk_next;
     }
-    for (; u < u1; ++u) iteration(u, flag_t<true>{}, ktile(u + 3), ktile(u + 2), nothing);
+    for (; u < u1; ++u) iteration(u, flag_t<true>{}, tile_rsrc(Kh, ktile(u + 3)), tile_rsrc(Vh, ktile(u + 2)), [] {});
   } else {
-    for (; u + 3 < u1; ++u) iteration(u, flag_t<false>{}, u + 3, u + 2, nothing);
-    for (; u < u1; ++u) iteration(u, flag_t<true>{}, u + 3, u + 2, nothing);
+    // the tiles at positions u + 3 (K) and u + 2 (V): addresses and rows left,
+    // advanced by one tile per iteration
+    const unsigned long long tile_bytes = (unsigned long long)64 * rowb;
+    unsigned long long ka = (unsigned long long)(Kh + (long long)(u0 + 3) * 64 * rowb);
+    unsigned long long va = (unsigned long long)(Vh + (long long)(u0 + 2) * 64 * rowb);
+    int kr = N - (u0 + 3) * 64, vr = N - (u0 + 2) * 64;
+    auto advance = [&]() __attribute__((always_inline)) {
+      ka += tile_bytes;
+      va += tile_bytes;
+      kr -= 64;
+      vr -= 64;
+    };
+    for (; u + 3 < u1; ++u) iteration(u, flag_t<false>{}, make_rsrc(ka, kr), make_rsrc(va, vr), advance);
+    for (; u < u1; ++u) iteration(u, flag_t<true>{}, make_rsrc(ka, kr), make_rsrc(va, vr), advance);
   }
 
   // ---- P V of the last sub-tile (its V fragments were read in the last phase Y)

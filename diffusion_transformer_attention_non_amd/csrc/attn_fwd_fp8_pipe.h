@@ -19,8 +19,8 @@
 //   from ds_read_b64_tr_b8 and P^T is packed from the S^T accumulators in the
 //   matching key order;
 // * probabilities are scaled by 2 before the e4m3 cast (the factor is added
-//   to the exponent argument): p down to 2^-8 of the running maximum stays
-//   in the normal e4m3 range, and p up to 232 times it fits (the maximum of
+//   to the exponent argument): p down to 2^-7 of the running maximum stays
+//   in the normal e4m3 range (2 p >= 2^-6), and p up to 232 times it fits (the maximum of
 //   the first sub-tile is usually a few bits below the row's). A power of
 //   two cancels in O. The row sums are those of the e4m3 values,
 //   taken on the matrix core (the output's denominator; the exact sums for

@@ -278,3 +278,49 @@ def test_build_refuses_spilling_attention_kernels():
     bad = ok.replace("ScratchSize [bytes/lane]: 0", "ScratchSize [bytes/lane]: 384")
     with pytest.raises(RuntimeError, match="attn_fwd_fp8_pipe_kernelX: 384"):
         check_no_spills(bad)
+
+
+def test_build_refuses_a_dma_reading_a_fresh_valu_written_sgpr():
+    """A VALU write of an SGPR needs 5 wait states before a buffer
+    instruction reads it (resource descriptor or soffset); the inline-asm LDS
+    DMA gets none from the compiler, so the build checks the ISA."""
+    from diffusion_transformer_attention_non_amd.build import check_vmem_sgpr_hazards
+    head = "_ZN7ditattn1kE:\n"
+    bad = head + ("\tv_readfirstlane_b32 s66, v1\n\t;;#ASMSTART\n"
+                  "\tbuffer_load_dwordx4 v233, s[64:67], 0 offen lds\n\t;;#ASMEND\n")
+    with pytest.raises(RuntimeError, match="s66"):
+        check_vmem_sgpr_hazards(bad)
+    # five wait states (instructions, or an s_nop 4) in between are enough
+    check_vmem_sgpr_hazards(head + "\tv_readfirstlane_b32 s66, v1\n\ts_nop 4\n"
+                            "\tbuffer_load_dwordx4 v233, s[64:67], 0 offen lds\n")
+    check_vmem_sgpr_hazards(head + "\tv_readfirstlane_b32 s66, v1\n" + "\ts_add_i32 s1, s1, 1\n" * 5 +
+                            "\tbuffer_load_dwordx4 v233, s[64:67], 0 offen lds\n")
+    with pytest.raises(RuntimeError):
+        check_vmem_sgpr_hazards(head + "\tv_readfirstlane_b32 s70, v1\n\ts_nop 2\n"
+                                "\tbuffer_load_dwordx4 v2, s[68:71], 0 offen lds\n")
+    # scalar writes and unrelated VALU-written SGPRs are fine
+    check_vmem_sgpr_hazards(head + "\ts_min_i32 s66, s66, 64\n\tv_readfirstlane_b32 s5, v1\n"
+                            "\tbuffer_load_dwordx4 v233, s[64:67], 0 offen lds\n")
+
+
+def test_inline_asm_that_writes_scc_declares_it():
+    """Scalar ALU instructions (compares, min/max, add/sub, shifts, logic) set
+    SCC. An inline-asm statement that contains one without declaring "scc"
+    clobbered lets the compiler keep a carry or compare result in SCC across
+    it: a 64-bit address add split by such an asm gets a wrong high word (a
+    GPU memory fault). Every asm statement of the kernels is checked."""
+    csrc = os.path.join(ROOT, "diffusion_transformer_attention_non_amd", "csrc")
+    writes_scc = re.compile(r"\bs_(cmp|min|max|add|sub|and|or|xor|lsh|ashr|bfe|bitcmp|absdiff|mul_hi)\w*")
+    checked = 0
+    for fn in sorted(os.listdir(csrc)):
+        text = open(os.path.join(csrc, fn)).read()
+        for m in re.finditer(r"\basm\s*(volatile\s*)?\(", text):
+            depth, k = 1, m.end()
+            while depth:
+                depth += {"(": 1, ")": -1}.get(text[k], 0)
+                k += 1
+            stmt = text[m.start():k]
+            checked += 1
+            if writes_scc.search(stmt):
+                assert '"scc"' in stmt, (fn, stmt[:200])
+    assert checked > 10
