@@ -251,28 +251,35 @@ void attn_fwd_fp8_pipe_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __r
     const int vc = vs ^ ((((vr >> 1) & 1) << 1) | (((vr >> 3) & 1) << 2));    // f(vr) is its own inverse
     vdo[m] = vr < C::kTileKeys ? vr * rowb + vc * 16 : C::kTileKeys * rowb;
   }
-  auto tile_rsrc = [&](const char* head, int t) __attribute__((always_inline)) {
-    const int rows = min(C::kTileKeys, N - t * C::kTileKeys);
-    const unsigned long long a = (unsigned long long)(head + (long long)t * C::kTileKeys * rowb);
+  // buffer descriptor of `rows` rows from address a: the range check
+  // zero-fills rows past them. Descriptors of tiles past the end are built
+  // but never read. Every field comes from the scalar unit: the inline-asm
+  // DMA reads it with no wait states of the compiler's in between.
+  auto make_rsrc = [&](unsigned long long a, int rows) __attribute__((always_inline)) {
     i32x4_t rs;
     rs[0] = __builtin_amdgcn_readfirstlane((int)(unsigned)a);
-    rs[1] = __builtin_amdgcn_readfirstlane((int)((a >> 32) & 0xffffu));
-    rs[2] = __builtin_amdgcn_readfirstlane(rows * rowb);
+    rs[1] = __builtin_amdgcn_readfirstlane((int)((a >> 32) & 0xffffu));   // stride 0
+    rs[2] = __builtin_amdgcn_readfirstlane(min(C::kTileKeys, rows) * rowb);
     rs[3] = 0x00020000;
     return rs;
+  };
+  auto tile_rsrc = [&](const char* head, int t) __attribute__((always_inline)) {
+    return make_rsrc((unsigned long long)(head + (long long)t * C::kTileKeys * rowb), N - t * C::kTileKeys);
   };
   // MX: instruction 4 of waves 2 and 3 (LDS bytes 18432.. and 19456.. of a K
   // slot) carries the tile's K scale words of keys 0-63 and 64-127, that of
   // every wave (16384.. of a V slot) its four V scale blocks; lanes past the
   // data zero-fill
-  auto bytes_rsrc = [&](const uint8_t* base, long long off, int bytes) __attribute__((always_inline)) {
-    const unsigned long long a = (unsigned long long)(base + off);
+  auto bytes_rsrc_at = [&](unsigned long long a, int bytes) __attribute__((always_inline)) {
     i32x4_t rs;
     rs[0] = __builtin_amdgcn_readfirstlane((int)(unsigned)a);
     rs[1] = __builtin_amdgcn_readfirstlane((int)((a >> 32) & 0xffffu));
     rs[2] = __builtin_amdgcn_readfirstlane(max(bytes, 0));
     rs[3] = 0x00020000;
     return rs;
+  };
+  auto bytes_rsrc = [&](const uint8_t* base, long long off, int bytes) __attribute__((always_inline)) {
+    return bytes_rsrc_at((unsigned long long)(base + off), bytes);
   };
   const int n_vb = (N + 31) / 32;
   auto kscale_rsrc = [&](int t) __attribute__((always_inline)) {
@@ -312,16 +319,17 @@ void attn_fwd_fp8_pipe_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __r
   const int k_rd = l32 * KROW + (MX ? hh * 16 : hh * 32);
   i32x8_t kf[2][2];                                     // [key block][d step]
   int ksc = 0;                                          // MX: the K scale word (bytes as qsc's)
-  auto read_kfrags = [&](int j) {
+  // K fragments of sub-tile `odd` (0, 1) of the 128-key tile in `slot`
+  auto read_kfrags = [&](const char* slot, int odd) {
     // MX: the scale words are read first, so that their permute waits for
     // them alone (LDS reads complete in order), not for the fragments
     int w0 = 0, w1 = 0;
     if constexpr (MX) {
-      const char* sb = kslot(j >> 1) + C::kKTile + (j & 1) * 1024 + l32 * 4;
+      const char* sb = slot + C::kKTile + odd * 1024 + l32 * 4;
       w0 = *(const int*)sb;
       w1 = *(const int*)(sb + 128);
     }
-    const char* kb = kslot(j >> 1) + (j & 1) * 64 * KROW + k_rd;
+    const char* kb = slot + odd * 64 * KROW + k_rd;
 #pragma unroll
     for (int b = 0; b < 2; ++b)
 #pragma unroll
@@ -344,10 +352,11 @@ void attn_fwd_fp8_pipe_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __r
   for (int db = 0; db < 4; ++db) v_rd[db] = tr_key * 128 + (((2 * db) ^ tr_gk) + (g & 1)) * 16 + (gi & 1) * 8;
   i32x8_t vf[4];                                        // [d block]
   int vsc = 0;                                          // MX: V scale word, byte db = column 32 db + l32
-  auto read_vfrags = [&](int j, int half) {             // half 0: d blocks 0, 1; half 1: 2, 3
-    const char* vb = vslot(j >> 1) + (j & 1) * 64 * 128;
+  // V fragments of sub-tile `odd` of the tile in `slot`; half 0: d blocks 0, 1; half 1: 2, 3
+  auto read_vfrags = [&](const char* slot, int odd, int half) {
+    const char* vb = slot + odd * 64 * 128;
     if constexpr (MX) {
-      if (half == 0) vsc = *(const int*)(vslot(j >> 1) + C::kVTile + ((j & 1) * 2 + hh) * 128 + l32 * 4);
+      if (half == 0) vsc = *(const int*)(slot + C::kVTile + (odd * 2 + hh) * 128 + l32 * 4);
     }
 #pragma unroll
     for (int db = half * 2; db < half * 2 + 2; ++db) {
@@ -437,6 +446,29 @@ void attn_fwd_fp8_pipe_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __r
   f32x16_t s0[2], s1[2];              // raw logits of the current sub-tile [query block][key block]
   i32x8_t pA[2], pB[2];               // P^T of two consecutive sub-tiles [query block]
 
+  // LDS byte offsets of the ring slots the iteration of tile u uses: K of
+  // tiles u, u+1, u+3 and V of u, u+2. They rotate by one slot per iteration
+  // (scalar adds instead of a modulo per use).
+  struct Ring {
+    int k0, k1, k3, v0, v2;
+  };
+  Ring ring;
+  {
+    auto rfl = [](int x) { return __builtin_amdgcn_readfirstlane(x); };
+    ring.k0 = rfl((u0 % C::kKSlots) * C::kSlot);
+    ring.k1 = rfl(((u0 + 1) % C::kKSlots) * C::kSlot);
+    ring.k3 = rfl(((u0 + 3) % C::kKSlots) * C::kSlot);
+    ring.v0 = rfl(C::kVBase + (u0 % C::kVSlots) * C::kSlot);
+    ring.v2 = rfl(C::kVBase + ((u0 + 2) % C::kVSlots) * C::kSlot);
+  }
+  auto advance_ring = [&]() __attribute__((always_inline)) {
+    ring.k3 = ring.k0;
+    ring.k0 = ring.k1;
+    ring.k1 = ring.k1 == (C::kKSlots - 1) * C::kSlot ? 0 : ring.k1 + C::kSlot;
+    ring.v2 = ring.v0;
+    ring.v0 = ring.v0 == C::kVBase + (C::kVSlots - 1) * C::kSlot ? C::kVBase : ring.v0 + C::kSlot;
+  };
+
   // ---- prologue: K tiles u0..u0+2, V tiles u0, u0+1; the first sub-tile's logits
   auto dma_ktile = [&](int t) __attribute__((always_inline)) {
     if constexpr (MX) {
@@ -465,7 +497,7 @@ void attn_fwd_fp8_pipe_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __r
   if (u0 + 1 < u1) dma_vtile(u0 + 1);
   __builtin_amdgcn_s_waitcnt(0x0F70);      // vmcnt(0)
   __syncthreads();
-  read_kfrags(2 * u0);
+  read_kfrags(kslot(u0), 0);
   s_chains(0, s0);
   s_chains(1, s1);
   if (64 * (2 * u0 + 1) > N) { mask_keys(2 * u0, s0); mask_keys(2 * u0, s1); }
@@ -485,7 +517,8 @@ void attn_fwd_fp8_pipe_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __r
     f32x4_t rs0, rs1;
     float ls0 = 0.f, ls1 = 0.f;
     // ================= phase X: P_{j-1} V_{j-1}, softmax of S_j block 0
-    read_kfrags(j + 1);
+    // the second sub-tile of a tile (j odd) takes the next K tile's first half
+    read_kfrags(smem + ((j & 1) ? ring.k1 : ring.k0), (j + 1) & 1);
     DIT_FENCE();
     {
       const float nm0 = kFp8PipePLog2 - mc[0];
@@ -537,7 +570,7 @@ void attn_fwd_fp8_pipe_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __r
         // were read a phase earlier); 8 at a time, lgkmcnt counts at most 15
         if (st < 2) {
           DIT_FENCE();
-          read_vfrags(j, st);
+          read_vfrags(smem + ring.v0, j & 1, st);
           DIT_FENCE();
         }
         if (st >= 4) dma(st - 4);
@@ -562,7 +595,7 @@ void attn_fwd_fp8_pipe_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __r
       // those registers keeps this path's working set to one accumulator
       // block, which keeps it from crowding the steady loop's registers.
       DIT_FENCE();
-      read_kfrags(j);                      // K tiles j/2 and (j+1)/2 are still in their slots
+      read_kfrags(smem + ring.k0, j & 1);  // K tiles j/2 and (j+1)/2 are still in their slots
       s_chains(0, s0);
       s_chains(1, s1);
       if constexpr (MASK) {
@@ -595,7 +628,7 @@ void attn_fwd_fp8_pipe_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __r
       }
       rs0 = psum(pout[0]);
       rs1 = psum(pout[1]);
-      read_kfrags(j + 1);
+      read_kfrags(smem + ((j & 1) ? ring.k1 : ring.k0), (j + 1) & 1);
       s_chains(0, s0);
       s_chains(1, s1);
       if constexpr (MASK) {
@@ -614,17 +647,16 @@ void attn_fwd_fp8_pipe_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __r
   // One 128-key tile u: streams in K tile u+3 (first sub-iteration) and V tile
   // u+2 (second), one DMA instruction per phase-Y step, then waits for the
   // tiles issued one iteration earlier before the barrier that publishes them.
-  auto iteration = [&](int u, auto tail_c) __attribute__((always_inline)) {
+  // rk, rv: the descriptors of the tiles at u + 3 (K) and u + 2 (V); rk4,
+  // rvs: those of the MX scale instructions; before_wait() runs after the
+  // compute, ahead of the wait (the next iteration's scalar bookkeeping goes
+  // there, behind the last MFMAs in flight).
+  auto iteration = [&](int u, auto tail_c, const i32x4_t& rk, const i32x4_t& rv, const i32x4_t& rk4,
+                       const i32x4_t& rvs, auto&& before_wait) __attribute__((always_inline)) {
     constexpr bool TAIL = decltype(tail_c)::value;
     const bool k_next = !TAIL || u + 3 < u1, v_next = !TAIL || u + 2 < u1;
-    const i32x4_t rk = tile_rsrc(Kh, u + 3), rv = tile_rsrc(Vh, u + 2);
-    i32x4_t rk4 = rk, rvs = rv;          // MX: the scale instructions' sources
-    if constexpr (MX) {
-      rk4 = wave >= 2 ? kscale_rsrc(u + 3) : rk;
-      rvs = vscale_rsrc(u + 2);
-    }
-    const char* sk = kslot(u + 3);
-    const char* sv = vslot(u + 2);
+    const char* sk = smem + ring.k3;
+    const char* sv = smem + ring.v2;
     DIT_FENCE();
     static_assert(C::kDmaPerWave == 5, "DMA hook spreads 5 instructions over 4 steps");
     sub(2 * u, pA, pB, tail_c, [&](int st) __attribute__((always_inline)) {
@@ -647,6 +679,8 @@ void attn_fwd_fp8_pipe_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __r
       }
     });
     DIT_FENCE();
+    before_wait();
+    advance_ring();
     if (TAIL)
       __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     else if (MX)
@@ -656,9 +690,43 @@ void attn_fwd_fp8_pipe_kernel(const uint8_t* __restrict__ Qg, const uint8_t* __r
     __syncthreads();
     DIT_FENCE();
   };
+  // the tiles at u + 3 (K) and u + 2 (V): addresses and rows left, and the
+  // MX scale blocks' addresses and bytes left, advanced by one tile per
+  // iteration
+  const unsigned long long tile_bytes = (unsigned long long)C::kTileKeys * rowb;
+  unsigned long long ka = (unsigned long long)(Kh + (long long)(u0 + 3) * C::kTileKeys * rowb);
+  unsigned long long va = (unsigned long long)(Vh + (long long)(u0 + 2) * C::kTileKeys * rowb);
+  int kr = N - (u0 + 3) * C::kTileKeys, vr = N - (u0 + 2) * C::kTileKeys;
+  unsigned long long ksa = 0, vsa = 0;
+  int vbr = 0;
+  if constexpr (MX) {
+    ksa = (unsigned long long)(mxs.k + ((long long)bh * N + (long long)(u0 + 3) * C::kTileKeys) * 4);
+    vsa = (unsigned long long)(mxs.v + ((long long)bh * n_vb + (long long)(u0 + 2) * 4) * 128);
+    vbr = n_vb - (u0 + 2) * 4;
+  }
+  auto advance = [&]() __attribute__((always_inline)) {
+    ka += tile_bytes;
+    va += tile_bytes;
+    kr -= C::kTileKeys;
+    vr -= C::kTileKeys;
+    if constexpr (MX) {
+      ksa += C::kTileKeys * 4;
+      vsa += 4 * 128;
+      vbr -= 4;
+    }
+  };
+  auto run = [&](int u, auto tail_c) __attribute__((always_inline)) {
+    const i32x4_t rk = make_rsrc(ka, kr), rv = make_rsrc(va, vr);
+    i32x4_t rk4 = rk, rvs = rv;          // MX: the scale instructions' sources
+    if constexpr (MX) {
+      rk4 = wave >= 2 ? bytes_rsrc_at(ksa, min(C::kTileKeys, kr) * 4) : rk;
+      rvs = bytes_rsrc_at(vsa, min(4, vbr) * 128);
+    }
+    iteration(u, tail_c, rk, rv, rk4, rvs, advance);
+  };
   int u = u0;
-  for (; u + 3 < u1; ++u) iteration(u, flag_t<false>{});
-  for (; u < u1; ++u) iteration(u, flag_t<true>{});
+  for (; u + 3 < u1; ++u) run(u, flag_t<false>{});
+  for (; u < u1; ++u) run(u, flag_t<true>{});
 
   // ---- P V of the last sub-tile (its V fragments were read in the last phase Y)
 #pragma unroll
