@@ -342,6 +342,18 @@ def main(argv=None):
                          "traffic": None}}
 
     if not args.no_extras:
+        # what the matrix cores sustain on changing random operands, right after the timed calls:
+        # the power-limited reference for the attention kernels on this card
+        ceil = {"bf16": dit.mfma_ceiling(dit.DIT_ATTN_BF16)}
+        ceil["bf16"]["frac"] = round(achieved / ceil["bf16"]["tflops"], 4)
+        if "fp8" in line:
+            ceil["fp8"] = dit.mfma_ceiling(dit.DIT_ATTN_FP8_E4M3)
+            ceil["fp8"]["frac"] = round(line["fp8"]["roofline"]["achieved"] / ceil["fp8"]["tflops"], 4)
+        ceil["kind"] = ("dit_attn_mfma_ceiling: independent 32x32 products back to back, one wave per SIMD, "
+                        "operands drawn from a counter hash and changing every product; frac = the kernel's "
+                        "achieved rate over this one")
+        line["mfma_ceiling"] = ceil
+
         # clocks under load: a thread reads them from a child process while
         # about four seconds of back-to-back calls run; a reading taken after
         # the queue drained (the stream already idle) is marked as such

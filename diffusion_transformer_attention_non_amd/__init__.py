@@ -15,7 +15,8 @@ from ._lib import (DIT_ATTN_BF16, DIT_ATTN_EDEVICE, DIT_ATTN_EINVAL, DIT_ATTN_EL
                    DIT_ATTN_EWORKSPACE, DIT_ATTN_NOALLOC_SCRATCH_BYTES, dit_attn_fwd_noalloc,
                    DIT_ATTN_MX_ALONG_D, DIT_ATTN_MX_ALONG_TOKENS, DIT_ATTN_OK, DIT_ATTN_SPARSE_KV_BLOCK,
                    DIT_ATTN_SPARSE_Q_BLOCK, DIT_ATTN_EUNSUPPORTED, dit_attn_fwd, dit_attn_fwd_blocksparse,
-                   dit_attn_fwd_ex, dit_attn_fwd_mx, dit_attn_fwd_strided, dit_attn_plan, dit_attn_quantize_e4m3,
+                   dit_attn_fwd_ex, dit_attn_fwd_mx, dit_attn_fwd_strided, dit_attn_mfma_ceiling, dit_attn_plan,
+                   dit_attn_quantize_e4m3,
                    dit_attn_quantize_mx, dit_attn_strerror, dit_attn_version, DitAttnPlan, DIT_ATTN_SCHED_SPLIT,
                    DIT_ATTN_SCHED_STREAMK, DIT_ATTN_SCHED_TILE)
 
@@ -27,7 +28,8 @@ __all__ = [
     "DIT_ATTN_SCHED_SPLIT", "DIT_ATTN_SCHED_STREAMK",
     "dit_attn_strerror", "dit_attn_version", "DIT_ATTN_BF16", "DIT_ATTN_FP8_E4M3", "DIT_ATTN_OK",
     "DIT_ATTN_EINVAL", "DIT_ATTN_EUNSUPPORTED", "DIT_ATTN_EDEVICE", "DIT_ATTN_ELAUNCH", "DIT_ATTN_EWORKSPACE",
-    "workspace_bytes", "dit_attn_fwd_noalloc", "DIT_ATTN_NOALLOC_SCRATCH_BYTES",
+    "workspace_bytes", "dit_attn_fwd_noalloc", "DIT_ATTN_NOALLOC_SCRATCH_BYTES", "dit_attn_mfma_ceiling",
+    "mfma_ceiling",
 ]
 
 
@@ -259,3 +261,38 @@ def quantize_e4m3(x, *, out=None, descale=None, workspace=None, stream=None):
     if st != DIT_ATTN_OK:
         raise DitAttnError(st, "dit_attn_quantize_e4m3")
     return out, descale
+
+
+def mfma_ceiling(dtype=DIT_ATTN_BF16, *, rounds=20000, reps=3, device=None):
+    """The matrix-core rate the current card sustains on attention-like
+    operands (dit_attn_mfma_ceiling): one warm-up launch, then ``reps`` timed
+    launches on the current stream. Returns a dict with ``tflops`` (median
+    launch), ``clock_mhz`` (shader clock over the product loops of that
+    launch) and ``cycles_per_product`` (32 for bf16, 64 for e4m3 when the
+    matrix cores never wait)."""
+    import torch
+    dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+    n_wg = torch.cuda.get_device_properties(dev).multi_processor_count
+    record = torch.zeros(n_wg * 8, dtype=torch.int64, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    flop = n_wg * 4 * rounds * 16 * (32 * 32 * 64 * 2 if dtype == DIT_ATTN_FP8_E4M3 else 32 * 32 * 16 * 2)
+    runs = []
+    for i in range(reps + 1):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        st, khz = dit_attn_mfma_ceiling(dtype, rounds, n_wg, record, record.numel() * 8, stream.cuda_stream)
+        e1.record(stream)
+        if st != DIT_ATTN_OK:
+            raise DitAttnError(st, "dit_attn_mfma_ceiling")
+        stream.synchronize()
+        if i == 0:
+            continue
+        rec = record.view(-1, 2).double()
+        cycles, ticks = rec[:, 0].sum().item(), rec[:, 1].sum().item()
+        ms = e0.elapsed_time(e1)
+        runs.append((flop / (ms * 1e-3) / 1e12, cycles / ticks * khz / 1000.0,
+                     cycles / (n_wg * 4) / (rounds * 16)))
+    runs.sort()
+    tflops, mhz, cpp = runs[len(runs) // 2]
+    return {"tflops": round(tflops, 1), "clock_mhz": round(mhz, 0), "cycles_per_product": round(cpp, 2),
+            "rounds": rounds, "workgroups": n_wg}

@@ -32,7 +32,7 @@ DIT_ATTN_SCHED_STREAMK = 2
 DIT_ATTN_NOALLOC_SCRATCH_BYTES = 68157440
 
 EXPORTED = ("dit_attn_fwd", "dit_attn_fwd_blocksparse", "dit_attn_fwd_ex", "dit_attn_fwd_mx", "dit_attn_fwd_noalloc",
-            "dit_attn_fwd_strided",
+            "dit_attn_fwd_strided", "dit_attn_mfma_ceiling",
             "dit_attn_plan", "dit_attn_quantize_e4m3", "dit_attn_quantize_mx", "dit_attn_strerror",
             "dit_attn_version")
 
@@ -72,6 +72,8 @@ _lib.dit_attn_quantize_e4m3.argtypes = [_vp, _i64, _vp, _vp, _vp, _vp]
 _lib.dit_attn_quantize_e4m3.restype = _i
 _lib.dit_attn_strerror.argtypes = [_i]
 _lib.dit_attn_strerror.restype = ctypes.c_char_p
+_lib.dit_attn_mfma_ceiling.argtypes = [_i, _i, _i, _vp, _i64, ctypes.POINTER(ctypes.c_int), _vp]
+_lib.dit_attn_mfma_ceiling.restype = _i
 _lib.dit_attn_version.argtypes = []
 _lib.dit_attn_version.restype = _i
 
@@ -157,3 +159,11 @@ def dit_attn_strerror(status: int) -> str:
 
 def dit_attn_version() -> int:
     return _lib.dit_attn_version()
+
+
+def dit_attn_mfma_ceiling(dtype, rounds, workgroups, record, record_bytes, stream=None):
+    """Returns (status, wall-clock tick rate in kHz)."""
+    khz = ctypes.c_int(0)
+    st = _lib.dit_attn_mfma_ceiling(dtype, rounds, workgroups, _ptr(record), int(record_bytes), ctypes.byref(khz),
+                                    _ptr(stream))
+    return st, khz.value

@@ -14,6 +14,7 @@
 #include "attn_fwd_fp8_pipe.h"
 #include "quant_e4m3.h"
 #include "quant_mx.h"
+#include "mfma_ceiling.h"
 
 using namespace ditattn;
 
@@ -77,6 +78,10 @@ int check_device() {
     if (allow_lds_pipe<CfgBf16D128>() != hipSuccess || allow_lds_bf16<CfgBf16D64>() != hipSuccess ||
         allow_lds_fp8<CfgFp8D128>() != hipSuccess)
       return DIT_ATTN_EDEVICE;
+    for (const void* k : {reinterpret_cast<const void*>(&mfma_ceiling_kernel<false>),
+                          reinterpret_cast<const void*>(&mfma_ceiling_kernel<true>)})
+      if (hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, kCeilingLds) != hipSuccess)
+        return DIT_ATTN_EDEVICE;
   }
   if (ok && dev < kMaxDevices) {
     int n_cu = 0;
@@ -465,7 +470,33 @@ int plan_kind(int d, int dtype, int max_blocks) {
 
 extern "C" {
 
-int dit_attn_version(void) { return (2 << 16) | 0; }
+int dit_attn_version(void) { return (2 << 16) | 1; }
+
+int dit_attn_mfma_ceiling(int dtype, int rounds, int workgroups, void* record, int64_t record_bytes,
+                          int* wall_clock_khz, void* stream) {
+  if (rounds < 1 || workgroups < 0 || workgroups > (1 << 20) || record == nullptr || record_bytes < 0 ||
+      !aligned(record, 8))
+    return DIT_ATTN_EINVAL;
+  if (dtype != DIT_ATTN_BF16 && dtype != DIT_ATTN_FP8_E4M3) return DIT_ATTN_EUNSUPPORTED;
+  const int dev_status = check_device();
+  if (dev_status != DIT_ATTN_OK) return dev_status;
+  const int wg = workgroups > 0 ? workgroups : cu_count();
+  if (record_bytes < (int64_t)wg * 4 * 2 * (int64_t)sizeof(long long)) return DIT_ATTN_EWORKSPACE;
+  if (wall_clock_khz != nullptr) {
+    int dev = 0, khz = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess || khz <= 0)
+      return DIT_ATTN_EDEVICE;
+    *wall_clock_khz = khz;
+  }
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  long long* rec = static_cast<long long*>(record);
+  if (dtype == DIT_ATTN_FP8_E4M3)
+    hipLaunchKernelGGL(mfma_ceiling_kernel<true>, dim3((unsigned)wg), dim3(256), kCeilingLds, st, rec, rounds);
+  else
+    hipLaunchKernelGGL(mfma_ceiling_kernel<false>, dim3((unsigned)wg), dim3(256), kCeilingLds, st, rec, rounds);
+  return hipGetLastError() == hipSuccess ? DIT_ATTN_OK : DIT_ATTN_ELAUNCH;
+}
 
 const char* dit_attn_strerror(int status) {
   switch (status) {

@@ -343,9 +343,42 @@ DIT_ATTN_API int dit_attn_plan(int B, int H, int N, int d, int dtype, int max_bl
 /* Human-readable name of a status code (static string, never NULL). */
 DIT_ATTN_API const char* dit_attn_strerror(int status);
 
+/*
+ * dit_attn_mfma_ceiling - the matrix-core rate this card sustains on
+ * attention-like operands, for setting an attention call against it.
+ *
+ * The dense MFMA peaks assume the 2.4 GHz peak engine clock. A stream of
+ * products whose operands change from product to product drives the part to
+ * its power limit below that clock, by an amount that depends on the data;
+ * the attention kernels run into the same limit. This launches `workgroups`
+ * workgroups of four waves (one wave per SIMD; 0 = one per CU), each wave
+ * issuing rounds x 16 independent products back to back on operands drawn
+ * once from a fixed counter hash: v_mfma_f32_32x32x16_bf16 on bf16 values of
+ * about unit variance (dtype DIT_ATTN_BF16, 32768 flop per product) or
+ * v_mfma_scale_f32_32x32x64_f8f6f4 on normal e4m3 codes at scale 2^0 (dtype
+ * DIT_ATTN_FP8_E4M3, 131072 flop per product). It measures no attention
+ * and follows no passage of the pages: it is the reference point for the
+ * measurement of the attention calls.
+ * record         : device buffer of at least workgroups x 64 bytes (int64,
+ *                  8-byte aligned), caller-owned. Wave w = 4 workgroup +
+ *                  wave index writes record[2 w] = shader-clock cycles
+ *                  (s_memtime) and record[2 w + 1] = wall-clock ticks
+ *                  (s_memrealtime) over its product loop; cycles / ticks x
+ *                  wall_clock_khz is the shader clock in kHz.
+ * wall_clock_khz : host pointer or NULL; receives the wall-clock tick rate.
+ * The caller times the launch (events on `stream`) for the rate in flop/s.
+ * Status: DIT_ATTN_EINVAL (rounds < 1, workgroups < 0 or > 2^20, NULL or
+ * misaligned record), DIT_ATTN_EUNSUPPORTED (dtype), DIT_ATTN_EDEVICE,
+ * DIT_ATTN_EWORKSPACE (record smaller than workgroups x 64 bytes),
+ * DIT_ATTN_ELAUNCH.
+ */
+DIT_ATTN_API int dit_attn_mfma_ceiling(int dtype, int rounds, int workgroups, void* record, int64_t record_bytes,
+                          int* wall_clock_khz, void* stream);
+
 /* Library ABI version: (major << 16) | minor. 2.0: caller-owned workspaces
    (dit_attn_fwd_strided, _blocksparse and _mx take one; dit_attn_plan takes
-   its size and reports the schedule it buys); nothing allocates. */
+   its size and reports the schedule it buys); nothing allocates. 2.1:
+   dit_attn_mfma_ceiling. */
 DIT_ATTN_API int dit_attn_version(void);
 
 #ifdef __cplusplus

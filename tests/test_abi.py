@@ -24,7 +24,8 @@ def lib():
 
 def test_header_declares_the_entry_points():
     assert _declared() == sorted(["dit_attn_fwd", "dit_attn_fwd_blocksparse", "dit_attn_fwd_ex", "dit_attn_fwd_mx",
-                                  "dit_attn_fwd_noalloc", "dit_attn_fwd_strided", "dit_attn_plan", "dit_attn_quantize_e4m3",
+                                  "dit_attn_fwd_noalloc", "dit_attn_fwd_strided", "dit_attn_mfma_ceiling", "dit_attn_plan",
+                                  "dit_attn_quantize_e4m3",
                                   "dit_attn_quantize_mx", "dit_attn_strerror", "dit_attn_version"])
 
 
@@ -259,11 +260,23 @@ def test_quantize_rejects_bad_arguments(lib):
     assert lib.dit_attn_quantize_e4m3(A, 64, B_, O, O, None) == -1      # descale aliases ws
 
 
+def test_mfma_ceiling_rejects_bad_arguments(lib):
+    f = lib.dit_attn_mfma_ceiling
+    assert f(0, 0, 1, A, 64)[0] == -1             # rounds < 1
+    assert f(0, 10, -1, A, 64)[0] == -1           # workgroups < 0
+    assert f(0, 10, (1 << 20) + 1, A, 1 << 30)[0] == -1
+    assert f(0, 10, 1, 0, 64)[0] == -1            # NULL record
+    assert f(0, 10, 1, A + 4, 64)[0] == -1        # misaligned record
+    assert f(0, 10, 1, A, -1)[0] == -1
+    assert f(7, 10, 1, A, 64)[0] == -2            # dtype
+
+
 def test_valid_call_without_gpu_reports_device_error(lib):
     import torch
     if torch.cuda.is_available():
         pytest.skip("a GPU is present; covered by the GPU tests")
     assert lib.dit_attn_fwd(A, B_, C, O, 1, 1, 8, 64, 0.125, 0, None) == -3
+    assert lib.dit_attn_mfma_ceiling(0, 10, 1, A, 64)[0] == -3
 
 
 def test_build_refuses_spilling_attention_kernels():
