@@ -47,13 +47,17 @@ def _f64(x) -> np.ndarray:
     return np.asarray(x, dtype=np.float64)
 
 
-def attention(q, k, v, scale: float, rows=None, block: int = 512, want_abs: bool = False):
-    """Return ``(O, lse)`` (and ``A`` if ``want_abs``) in float64.
+def attention(q, k, v, scale: float, rows=None, block: int = 512, want_abs: bool = False,
+              want_sq: bool = False):
+    """Return ``(O, lse)`` (then ``A`` if ``want_abs``, then ``M2`` if
+    ``want_sq``) in float64.
 
     q, k, v: (B, H, N, d) arrays or tensors. ``rows``: optional index array
     of query rows to evaluate (the same rows for every (b, h)); the outputs
-    then have R = len(rows) rows. ``A[b,h,i,c] = sum_j p_ij |V[b,h,j,c]|`` is
-    the weighted absolute value used to bound the effect of rounding p.
+    then have R = len(rows) rows. ``A[b,h,i,c] = sum_j p_ij |V[b,h,j,c]|`` and
+    ``M2[b,h,i,c] = sum_j p_ij V[b,h,j,c]^2`` are the weighted absolute value
+    and second moment of V's column under row i's weights; they bound the
+    effect of rounding p (test infrastructure, not part of the operation).
     """
     q, k, v = _f64(q), _f64(k), _f64(v)
     B, H, N, d = q.shape
@@ -63,11 +67,13 @@ def attention(q, k, v, scale: float, rows=None, block: int = 512, want_abs: bool
     out = np.empty((B, H, R, d))
     lse = np.empty((B, H, R))
     absw = np.empty((B, H, R, d)) if want_abs else None
+    sqw = np.empty((B, H, R, d)) if want_sq else None
     for b in range(B):
         for h in range(H):
             kt = k[b, h].T
             vb = v[b, h]
             va = np.abs(vb) if want_abs else None
+            vs = vb * vb if want_sq else None
             for r0 in range(0, R, block):
                 sel = idx[r0:r0 + block]
                 s = (q[b, h, sel] @ kt) * scale          # logits of these rows
@@ -78,9 +84,14 @@ def attention(q, k, v, scale: float, rows=None, block: int = 512, want_abs: bool
                 lse[b, h, r0:r0 + sel.size] = m[:, 0] + np.log(den[:, 0])
                 if want_abs:
                     absw[b, h, r0:r0 + sel.size] = (e @ va) / den
+                if want_sq:
+                    sqw[b, h, r0:r0 + sel.size] = (e @ vs) / den
+    res = (out, lse)
     if want_abs:
-        return out, lse, absw
-    return out, lse
+        res += (absw,)
+    if want_sq:
+        res += (sqw,)
+    return res
 
 
 def softmax_probabilities(q, k, scale: float) -> np.ndarray:

@@ -2,16 +2,26 @@
 and compare it with the oracle on the same seeded inputs.
 
 bf16 output, every compared element (float64 arithmetic), u = 2^-8 the unit
-roundoff of bf16 (8 significant bits):
+roundoff of bf16 (8 significant bits), w_j = p_ij the exact weights of row i,
+A = sum_j w_j |V_jc|, M2 = sum_j w_j V_jc^2 (both from the oracle):
 * spec: max |O_gpu - O| <= 2e-2 and mean |O_gpu - O| <= 2e-3.
-* derived bound: |O_gpu - O| <= u (A + |O|)(1 + 2^-6) + 2^-12 A + 1e-6, with
-  A = sum_j p_ij |V_jc|. The kernels round each probability to bf16
-  (p~_j = p_j (1 + e_j), |e_j| <= u) before the PV product and divide by the
-  fp32 sum of the unrounded p_j, so the weights move by p_j e_j / sum p: at
-  most u A on the output. Rounding the output to bf16 adds u |O|. The fp32
-  parts (logits from the MFMA, exp2, sums over N/16 chained products) move a
-  weight by far less than 2^-14 relative, which the (1 + 2^-6) factor covers;
-  2^-12 A is slack.
+* derived bound (bf16_bound):
+      |O_gpu - O| <= (u (1 + 2^-6) + 2^-20 L) D + u |O|
+                     + (N/16 + 48) 2^-24 (A + |O|) + 2^-12 A + 1e-6,
+      D = min(A + |O|, sqrt(max(M2 - O^2, 0))).
+  The kernels round each probability to bf16 (p~_j = p_j (1 + e_j),
+  |e_j| <= u) and divide the P V product by the sum of the same rounded p~_j,
+  so the weights become w_j (1 + e_j) / (1 + e), e = sum_j w_j e_j, and O
+  moves by sum_j w_j e_j (V_j - O) / (1 + e): at most u (1 + 2^-7) D, where
+  sum_j w_j |V_j - O| is at most A + |O| and, by Jensen, at most the weighted
+  standard deviation sqrt(M2 - O^2). A logit carries at most 2^-21 L of fp32
+  error (L = scale |q_i| max_j |k_j|, see logit_scale; 8 roundings of the
+  MFMA chain, plus the exponent argument's own rounding and exp2's), which
+  moves a weight by at most 2^-20 L relative, again against V_j - O (a common
+  shift of every logit cancels). Rounding the output to bf16 adds u |O|. The
+  fp32 sums (the PV accumulator over N/16 chained 16-term products, the row
+  sum of the rounded P over N/32 sub-tiles of 32-term products, the final
+  reciprocal) add at most (N/16 + 48) 2^-24 (A + |O|); 2^-12 A is slack.
 * log-sum-exp (see lse_tolerance): the row sum is an fp32 sum of N terms in
   two levels (16 per lane and sub-tile, then N/32 partial sums, then the
   half-wave pair), relative error at most (16 + N/32 + 8) 2^-24; a logit
@@ -69,8 +79,15 @@ def gpu_attention(q, k, v, scale, want_lse=False):
     return o.float().cpu().double().numpy(), (lse.cpu().double().numpy() if want_lse else None)
 
 
-def bf16_bound(o_ref, a_ref):
-    return U_BF16 * (a_ref + np.abs(o_ref)) * (1 + 2.0**-6) + 2.0**-12 * a_ref + 1e-6
+def bf16_bound(o_ref, a_ref, n_keys, m2_ref=None, logit_mag=None):
+    """The derived per-element bound of the module docstring. o_ref, a_ref,
+    m2_ref: (B, H, R, d); logit_mag: (B, H, R) (logit_scale) or None for
+    logits of unit size; n_keys: keys each row attends to."""
+    ao = a_ref + np.abs(o_ref)
+    dev = ao if m2_ref is None else np.minimum(ao, np.sqrt(np.maximum(m2_ref - o_ref * o_ref, 0.0)))
+    lm = 1.0 if logit_mag is None else np.asarray(logit_mag)[..., None]
+    return (U_BF16 * (1 + 2.0**-6) + 2.0**-20 * lm) * dev + U_BF16 * np.abs(o_ref) \
+        + (n_keys / 16 + 48) * 2.0**-24 * ao + 2.0**-12 * a_ref + 1e-6
 
 
 def _f64(x):
@@ -97,10 +114,10 @@ def check_lse(l_gpu, l_ref, tol, label=""):
     assert (err <= tol).all(), (label, float(err.max()), float((err / tol).max()))
 
 
-def check_bf16(o_gpu, o_ref, a_ref, label=""):
+def check_bf16(o_gpu, o_ref, a_ref, label="", *, n_keys, m2_ref=None, logit_mag=None):
     err = np.abs(o_gpu - o_ref)
     mx, mean = float(err.max()), float(err.mean())
-    bound = bf16_bound(o_ref, a_ref)
+    bound = bf16_bound(o_ref, a_ref, n_keys, m2_ref, logit_mag)
     worst = float((err / bound).max())
     say(f"  {label}: max {mx:.3e} mean {mean:.3e} worst err/bound {worst:.3f}")
     assert np.isfinite(o_gpu).all(), label
@@ -110,23 +127,30 @@ def check_bf16(o_gpu, o_ref, a_ref, label=""):
 
 
 def check_full(o_gpu, l_gpu, q, k, scale, ref, label, rows=None):
-    """bf16 output and LSE against an oracle result ref = (O, lse, A)."""
-    o_ref, l_ref, a_ref = ref
-    check_bf16(o_gpu, o_ref, a_ref, label)
+    """bf16 output and LSE against an oracle result ref = (O, lse, A[, M2])."""
+    o_ref, l_ref, a_ref = ref[:3]
+    m2_ref = ref[3] if len(ref) > 3 else None
+    lm = logit_scale(q, k, scale, rows)
+    check_bf16(o_gpu, o_ref, a_ref, label, n_keys=q.shape[2], m2_ref=m2_ref, logit_mag=lm)
     if l_gpu is not None:
-        tol = lse_tolerance(q.shape[2], l_ref, logit_scale(q, k, scale, rows))
+        tol = lse_tolerance(q.shape[2], l_ref, lm)
         check_lse(l_gpu, l_ref, tol, label)
+
+
+def oracle_ref(q, k, v, scale, rows=None):
+    """(O, lse, A, M2) of the fp64 oracle: what check_full takes."""
+    return oracle.attention(q, k, v, scale, rows=rows, want_abs=True, want_sq=True)
 
 
 @functools.lru_cache(maxsize=2)
 def oracle_workload(name: str):
-    """The fp64 oracle (O, lse, A) on every row of a named workload, computed
+    """The fp64 oracle (O, lse, A, M2) on every row of a named workload, computed
     once per test session (the bf16 and fp8 tests of one shape share it)."""
     from workloads import WORKLOADS, make_qkv
     w = WORKLOADS[name]
     q, k, v = make_qkv(w)
     say(f"  oracle on every row of {name} (B={w.B} H={w.H} N={w.N} d={w.d}) ...")
-    return oracle.attention(q, k, v, 1.0 / np.sqrt(w.d), want_abs=True)
+    return oracle.attention(q, k, v, 1.0 / np.sqrt(w.d), want_abs=True, want_sq=True)
 
 
 def fp8_bound(q, k, v, scale, o_emul, rows=None, block=512, z=Z_FP8):

@@ -6,7 +6,7 @@ import pytest
 import torch
 
 import oracle
-from parity import check_bf16, check_full, gpu_attention, oracle_workload, say
+from parity import check_bf16, check_full, gpu_attention, logit_scale, oracle_ref, oracle_workload, say
 from workloads import (WORKLOADS, coverage_pattern, constant_values, dominating_key, identical_keys,
                        make_qkv, random_qkv)
 
@@ -16,7 +16,7 @@ pytestmark = pytest.mark.gpu
 def _full_check(q, k, v, scale, label, lse=True):
     say(f"[gpu] {label}: shape {tuple(q.shape)}")
     o, l = gpu_attention(q, k, v, scale, want_lse=lse)
-    check_full(o, l, q, k, scale, oracle.attention(q, k, v, scale, want_abs=True), label)
+    check_full(o, l, q, k, scale, oracle_ref(q, k, v, scale), label)
     return o
 
 
@@ -119,9 +119,12 @@ def test_joint_key_value_permutation_and_query_permutation():
     o, _ = gpu_attention(q, k, v, scale)
     o_k, _ = gpu_attention(q, k[:, :, pk].contiguous(), v[:, :, pk].contiguous(), scale)
     o_q, _ = gpu_attention(q[:, :, pq].contiguous(), k, v, scale)
-    o_ref, _, a_ref = oracle.attention(q, k, v, scale, want_abs=True)
-    check_bf16(o_k, o_ref, a_ref, "K/V permuted")
-    check_bf16(o_q, o_ref[:, :, pq.numpy()], a_ref[:, :, pq.numpy()], "Q permuted")
+    o_ref, _, a_ref, m2_ref = oracle_ref(q, k, v, scale)
+    lm = logit_scale(q, k, scale)
+    check_bf16(o_k, o_ref, a_ref, "K/V permuted", n_keys=2000, m2_ref=m2_ref, logit_mag=lm)
+    pi = pq.numpy()
+    check_bf16(o_q, o_ref[:, :, pi], a_ref[:, :, pi], "Q permuted", n_keys=2000, m2_ref=m2_ref[:, :, pi],
+               logit_mag=lm[:, :, pi])
     assert np.abs(o_k - o).max() <= 2 * (2.0**-8) * (np.abs(o_ref).max() + a_ref.max())
 
 
@@ -138,8 +141,9 @@ def test_deterministic_and_heads_independent():
     assert np.array_equal(o_one[0, 0], o1[1, 2])
     # a different batch shape: other key ranges, same values to within rounding
     o_pair, _ = gpu_attention(q[1:2].contiguous(), k[1:2].contiguous(), v[1:2].contiguous(), scale)
-    o_ref, _, a_ref = oracle.attention(q[1:2], k[1:2], v[1:2], scale, want_abs=True)
-    check_bf16(o_pair, o_ref, a_ref, "B=1 H=3 slice")
+    o_ref, _, a_ref, m2_ref = oracle_ref(q[1:2], k[1:2], v[1:2], scale)
+    check_bf16(o_pair, o_ref, a_ref, "B=1 H=3 slice", n_keys=1500, m2_ref=m2_ref,
+               logit_mag=logit_scale(q[1:2], k[1:2], scale))
     assert (np.abs(o_pair - o1[1:2]) <= 2 * (2.0**-8) * (np.abs(o_ref) + a_ref) + 1e-6).all()
 
 

@@ -54,7 +54,7 @@ def _compare(q, k, v, blocks, counts, scale, label, rows=None):
         og, lg = og[:, :, rows], lg[:, :, rows]
     empty = np.isneginf(l_ref)
     assert np.all(og[empty] == 0.0), label
-    check_bf16(og, o_ref, a_ref, label)
+    check_bf16(og, o_ref, a_ref, label, n_keys=q.shape[2], logit_mag=logit_scale(q, k, scale, rows))
     tol = lse_tolerance(q.shape[2], np.where(empty, 0.0, l_ref), logit_scale(q, k, scale, rows))
     _check_lse(lg, l_ref, tol, label)
     return o, l

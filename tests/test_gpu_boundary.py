@@ -10,7 +10,7 @@ import pytest
 import torch
 
 import oracle
-from parity import check_bf16, check_lse, say
+from parity import check_bf16, check_lse, logit_scale, oracle_ref, say
 from workloads import WORKLOADS, make_qkv, random_qkv, sample_rows
 
 pytestmark = pytest.mark.gpu
@@ -58,11 +58,12 @@ def test_short_form_without_workspace(name):
     _call(dit, qd, kd, vd, o_ws, scale, ws=ws, ws_bytes=nbytes)
     torch.cuda.synchronize()
     rows = sample_rows(N, seed=7, n_edge=128, stride=64)
-    o_ref, _, a_ref = oracle.attention(q, k, v, scale, rows=rows, want_abs=True)
+    o_ref, _, a_ref, m2_ref = oracle_ref(q, k, v, scale, rows=rows)
+    kw = dict(n_keys=N, m2_ref=m2_ref, logit_mag=logit_scale(q, k, scale, rows))
     a = o_short.float().cpu().double().numpy()
     b = o_ws.float().cpu().double().numpy()
-    check_bf16(a[:, :, rows], o_ref, a_ref, f"{name} no workspace")
-    check_bf16(b[:, :, rows], o_ref, a_ref, f"{name} workspace")
+    check_bf16(a[:, :, rows], o_ref, a_ref, f"{name} no workspace", **kw)
+    check_bf16(b[:, :, rows], o_ref, a_ref, f"{name} workspace", **kw)
 
 
 def test_undersized_workspace_is_refused_and_nothing_runs():

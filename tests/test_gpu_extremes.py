@@ -8,7 +8,8 @@ import pytest
 import torch
 
 import oracle
-from parity import (check_fp8_against_emulation, check_full, fp8_bound, gpu_attention, lse_tolerance, say)
+from parity import (check_fp8_against_emulation, check_full, fp8_bound, gpu_attention, lse_tolerance, oracle_ref,
+                    say)
 from workloads import random_qkv, sample_rows
 
 pytestmark = pytest.mark.gpu
@@ -22,7 +23,7 @@ def test_very_long_single_head(d):
     o, l = gpu_attention(q, k, v, 1 / math.sqrt(d), want_lse=True)
     rows = sample_rows(N, seed=3, n_edge=300, stride=400)
     check_full(o[:, :, rows], l[:, :, rows], q, k, 1 / math.sqrt(d),
-               oracle.attention(q, k, v, 1 / math.sqrt(d), rows=rows, want_abs=True), f"N={N} d={d}", rows=rows)
+               oracle_ref(q, k, v, 1 / math.sqrt(d), rows=rows), f"N={N} d={d}", rows=rows)
 
 
 @pytest.mark.parametrize("B,H,N,d", [(64, 48, 17, 128), (32, 40, 130, 64), (8, 96, 300, 128)])
@@ -30,7 +31,7 @@ def test_many_small_heads(B, H, N, d):
     q, k, v = random_qkv(B, H, N, d, seed=1200 + N)
     say(f"[gpu] many heads B={B} H={H} N={N} d={d}")
     o, l = gpu_attention(q, k, v, 1 / math.sqrt(d), want_lse=True)
-    check_full(o, l, q, k, 1 / math.sqrt(d), oracle.attention(q, k, v, 1 / math.sqrt(d), want_abs=True),
+    check_full(o, l, q, k, 1 / math.sqrt(d), oracle_ref(q, k, v, 1 / math.sqrt(d)),
                f"B={B} H={H} N={N} d={d}")
 
 

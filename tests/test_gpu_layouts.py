@@ -10,7 +10,7 @@ import pytest
 import torch
 
 import oracle
-from parity import check_full, say
+from parity import check_full, oracle_ref, say
 from workloads import WORKLOADS, make_qkv, random_qkv
 
 pytestmark = pytest.mark.gpu
@@ -68,7 +68,7 @@ def test_fused_qkv_against_oracle():
     qf, kf, vf = _fused_views(q, k, v, dev)
     o, l = _run(qf, kf, vf, scale)
     check_full(o.float().cpu().double().numpy(), l.cpu().double().numpy(), q, k, scale,
-               oracle.attention(q, k, v, scale, want_abs=True), "fused QKV (B=1 H=4 N=777)")
+               oracle_ref(q, k, v, scale), "fused QKV (B=1 H=4 N=777)")
 
 
 def test_fp8_bnhd_bitwise():

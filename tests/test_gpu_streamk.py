@@ -14,7 +14,7 @@ import pytest
 import torch
 
 import oracle
-from parity import check_bf16, check_full, gpu_attention, say
+from parity import check_bf16, check_full, gpu_attention, oracle_ref, say
 from workloads import coverage_pattern, random_qkv, sample_rows
 
 pytestmark = pytest.mark.gpu
@@ -27,7 +27,7 @@ def test_streamk_every_row(B, H, N):
     q, k, v = random_qkv(B, H, N, 128, seed=900 + H)
     say(f"[gpu] stream-K B={B} H={H} N={N}, every row")
     o, l = gpu_attention(q, k, v, 1 / math.sqrt(128), want_lse=True)
-    check_full(o, l, q, k, 1 / math.sqrt(128), oracle.attention(q, k, v, 1 / math.sqrt(128), want_abs=True),
+    check_full(o, l, q, k, 1 / math.sqrt(128), oracle_ref(q, k, v, 1 / math.sqrt(128)),
                f"stream-K H={H} N={N}")
 
 

@@ -160,6 +160,33 @@ def test_oracle_weighted_abs_and_row_sums():
     assert np.allclose(ones, 1.0, rtol=0, atol=1e-14)
 
 
+def test_oracle_weighted_second_moment():
+    """M2 = sum_j p_ij v_jc^2, pinned by literal loops (math.fsum, no matrix
+    product), the variance identity sum_j p_ij (v_jc - O_ic)^2 = M2 - O^2,
+    a constant column (M2 = c^2) and a one-hot row (M2 = v_jc^2)."""
+    q, k, v = _rand((1, 1, 12, 4), 94), _rand((1, 1, 12, 4), 95), _rand((1, 1, 12, 4), 96)
+    o, _, m2 = oracle.attention(q, k, v, 0.7, want_sq=True)
+    s = [[0.7 * math.fsum(q[0, 0, i, c] * k[0, 0, j, c] for c in range(4)) for j in range(12)] for i in range(12)]
+    for i in range(12):
+        mx = max(s[i])
+        w = [math.exp(x - mx) for x in s[i]]
+        den = math.fsum(w)
+        for c in range(4):
+            sq = math.fsum(w[j] * v[0, 0, j, c] ** 2 for j in range(12)) / den
+            var = math.fsum(w[j] * (v[0, 0, j, c] - o[0, 0, i, c]) ** 2 for j in range(12)) / den
+            assert abs(m2[0, 0, i, c] - sq) <= 1e-13 * max(1.0, sq)
+            assert abs((m2[0, 0, i, c] - o[0, 0, i, c] ** 2) - var) <= 1e-12
+    vc = np.tile(np.array([2.0, -3.0, 0.5, 0.0]), (1, 1, 12, 1))
+    _, _, a2, m2c = oracle.attention(q, k, vc, 0.7, want_abs=True, want_sq=True)
+    assert np.allclose(m2c, vc[:, :, :1] ** 2, rtol=0, atol=1e-13)
+    assert np.allclose(a2, np.abs(vc[:, :, :1]), rtol=0, atol=1e-13)
+    kp = np.zeros((1, 1, 12, 4))
+    kp[0, 0, 5, 0] = 1e3               # key 5 dominates every row with q[..., 0] > 0
+    qp = np.abs(q) + 0.1
+    _, _, m2p = oracle.attention(qp, kp, v, 1.0, want_sq=True)
+    assert np.allclose(m2p, np.broadcast_to(v[:, :, 5:6] ** 2, m2p.shape), rtol=1e-12, atol=1e-12)
+
+
 def test_oracle_accepts_bf16_tensors_exactly():
     q, k, v = random_qkv(1, 1, 20, 8, seed=3)
     o, _ = oracle.attention(q, k, v, 0.35)

@@ -10,7 +10,7 @@ import numpy as np
 import pytest
 
 import oracle
-from parity import bf16_bound, check_fp8_against_emulation, fp8_bound
+from parity import bf16_bound, check_fp8_against_emulation, fp8_bound, logit_scale
 from workloads import random_qkv
 
 
@@ -60,18 +60,39 @@ def _bf16_model(q, k, v, scale, mistake=None):
             pr = oracle.bf16_round(p)
             if mistake == "one key dropped":
                 pr[:, N // 2] = 0
-            den = (pr if mistake == "rounded denominator, output not rounded" else p).sum(axis=1, keepdims=True)
-            o = (pr @ v[b, h]) / den
-            out[b, h] = o if mistake == "rounded denominator, output not rounded" else oracle.bf16_round(o)
+            # the kernels' arithmetic: bf16 P, divided by the sum of the same rounded P
+            out[b, h] = oracle.bf16_round((pr @ v[b, h]) / pr.sum(axis=1, keepdims=True))
     return out
 
 
 def test_bf16_bound_passes_the_model_and_fails_a_dropped_key():
     q, k, v = random_qkv(1, 2, 1000, 128, seed=77)
     scale = 1 / math.sqrt(128)
-    o_ref, _, a_ref = oracle.attention(q, k, v, scale, want_abs=True)
-    bound = bf16_bound(o_ref, a_ref)
-    err = np.abs(_bf16_model(q, k, v, scale) - o_ref)
-    assert (err <= bound).all(), float((err / bound).max())
-    err = np.abs(_bf16_model(q, k, v, scale, "one key dropped") - o_ref)
-    assert not (err <= bound).all()
+    o_ref, _, a_ref, m2_ref = oracle.attention(q, k, v, scale, want_abs=True, want_sq=True)
+    lm = logit_scale(q, k, scale)
+    for m2 in (None, m2_ref):
+        bound = bf16_bound(o_ref, a_ref, 1000, m2, lm)
+        err = np.abs(_bf16_model(q, k, v, scale) - o_ref)
+        assert (err <= bound).all(), float((err / bound).max())
+        err = np.abs(_bf16_model(q, k, v, scale, "one key dropped") - o_ref)
+        assert not (err <= bound).all()
+
+
+def test_bf16_bound_covers_rounding_errors_aligned_with_the_values():
+    """Dividing by the sum of the rounded P moves O by sum_j w_j e_j (V_j - O),
+    which can exceed u (A + |O|): here 2 keys of value 10 whose p round up
+    and 63 keys of value 0 whose p round down (all p in [1, 2), so each
+    rounding error is chosen by its p). The derived bound holds; a bound of
+    u (A + |O|)(1 + 2^-6) would not."""
+    u = 2.0**-8
+    p = np.array([1 + 0.51 * 2.0**-7] * 2 + [1 + 1.49 * 2.0**-7] * 63)
+    v = np.array([10.0] * 2 + [0.0] * 63)
+    w = p / p.sum()
+    o, a, m2 = w @ v, w @ np.abs(v), w @ (v * v)
+    pr = oracle.bf16_round(p)
+    got = oracle.bf16_round((pr @ v) / pr.sum())
+    err = abs(got - o)
+    narrow = u * (a + abs(o)) * (1 + 2.0**-6) + 2.0**-12 * a + 1e-6
+    assert err > narrow
+    bound = bf16_bound(np.array([[[[o]]]]), np.array([[[[a]]]]), 65, np.array([[[[m2]]]]))
+    assert err <= float(bound.ravel()[0])

@@ -10,7 +10,7 @@ import pytest
 import torch
 
 import oracle
-from parity import check_full, say
+from parity import check_full, oracle_ref, say
 from workloads import random_qkv, sample_rows
 
 pytestmark = pytest.mark.gpu
@@ -63,7 +63,7 @@ def test_noalloc_matches_the_workspace_entry_point_on_consecutive_calls(shapes):
         rows = sample_rows(N, seed=i, n_edge=128, stride=32)
         o = o_na.float().cpu().double().numpy()[:, :, rows]
         l = l_na.cpu().double().numpy()[:, :, rows]
-        check_full(o, l, q, k, scale, oracle.attention(q, k, v, scale, rows=rows, want_abs=True),
+        check_full(o, l, q, k, scale, oracle_ref(q, k, v, scale, rows=rows),
                    f"noalloc B={B} H={H} N={N}", rows=rows)
 
 
@@ -80,7 +80,7 @@ def test_noalloc_fp8_then_smaller_bf16():
     (o_na, l_na), (o_ws, l_ws) = _both(q.to(DEV), k.to(DEV), v.to(DEV), 1 / math.sqrt(128))
     assert torch.equal(o_na, o_ws) and torch.equal(l_na, l_ws)
     check_full(o_na.float().cpu().double().numpy(), l_na.cpu().double().numpy(), q, k, 1 / math.sqrt(128),
-               oracle.attention(q, k, v, 1 / math.sqrt(128), want_abs=True), "noalloc B=1 H=2 N=3000")
+               oracle_ref(q, k, v, 1 / math.sqrt(128)), "noalloc B=1 H=2 N=3000")
 
 
 def test_noalloc_rejects_bad_arguments_before_launch():
