@@ -76,6 +76,10 @@ WORKLOADS = {
                             note="per-GPU share of t2i_2048 with 4-way head sharding"),
     "t2i_2048_h3": Workload("t2i_2048_h3", 1, 3, 16896, 128, 512, 16384,
                             note="per-GPU share of t2i_2048 with 8-way head sharding"),
+    # The head dimension of the tiny case at a full sequence: measures the
+    # d = 64 kernel (the workloads above are all d = 128).
+    "t2i_2048_d64": Workload("t2i_2048_d64", 1, 24, 16896, 64, 512, 16384,
+                             note="2048x2048-equivalent sequence at head dimension 64"),
 }
 
 
