@@ -25,19 +25,24 @@
 // of P_j and two FMAs forming exponent arguments (of S_j's second query block
 // in phase X, of S_{j+1}'s first in phase Y) behind the first, the row-sum
 // adds and the bf16 pack of those two exponentials behind the second, so that
-// no instruction waits on the transcendental unit's result. Fragment reads from LDS follow the MFMA that last reads
-// the register they fill: V_j over both phases, K_{j+2} over phase Y. P
-// alternates between two register sets over the two sub-iterations of a
-// tile, so nothing is copied at the loop edge. Row sums are fp32 adds: a
-// v_dot2 on the packed P would issue only after the MFMA in flight.
+// no instruction waits on the transcendental unit's result. Fragment reads
+// from LDS follow the MFMA that last reads the register they fill: V_j over
+// both phases, K_{j+2} over phase Y. P alternates between two register sets
+// over the two sub-iterations of a tile, so nothing is copied at the loop
+// edge. Row sums are of the rounded P (the values O is multiplied with), on
+// the matrix core: a 16x16x32 product of the packed P with a lane-selected
+// ones operand.
 //
 // Softmax without a per-tile maximum. The running maximum m (log2 units, per
 // query row) starts at the exact maximum of the first 32 keys. bf16 keeps
 // 8 significant bits at any scale, so probabilities relative to a stale m lose
-// nothing as long as nothing overflows: m moves only when a sum of 16 of a
-// sub-tile's probabilities exceeds 2^64 (or is not finite). That rare path
-// recomputes the sub-tile's logits from K (still in LDS), takes their exact
-// maximum, rescales O and l and recomputes P.
+// nothing as long as nothing overflows. A tile first runs with m fixed and no
+// test in the loop; its row sums are tested once at the end, and if any is
+// not finite or exceeds 2^64 the workgroup runs the tile again with the
+// checked loop, in which m moves whenever a sum of 16 of a sub-tile's
+// probabilities exceeds 2^64 (or is not finite): that rare path recomputes
+// the sub-tile's logits from K (still in LDS), takes their exact maximum,
+// rescales O and l and recomputes P.
 //
 // Row sums. O is divided by the sum of the bf16-rounded probabilities that
 // the P V products multiply V with, so every output row is a convex
@@ -77,7 +82,9 @@ struct PipeCfg {
   static constexpr int kSlot = kNW * kDmaPerWave * 1024;  // 20480
   static constexpr int kKSlots = 4, kVSlots = 3;
   static constexpr int kVBase = kKSlots * kSlot;
-  static constexpr int kLdsBytes = kVBase + kVSlots * kSlot;   // 143360
+  // past the slots: one word per wave, whether its unchecked pass overflowed
+  static constexpr int kFlagOff = kVBase + kVSlots * kSlot;   // 143360
+  static constexpr int kLdsBytes = kFlagOff + 16;
   static_assert(kKTile <= kSlot && kVTile <= kSlot, "tile fits its slot");
   // The bf16 O rows of a finished tile are staged in LDS (over the K/V slots,
   // 64 rows per wave, padded pitch) on their way to HBM.
@@ -364,300 +371,343 @@ __device__ __forceinline__ void pipe_tile(const uint16_t* __restrict__ Qg, const
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pt, c, 0, 0, 0);
   };
 
+  // The state a pass over the tile's keys leaves for the epilogue.
   f32x16_t acc[2][DB];
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[qb][db][r] = 0.f;
   float mc[2];                 // running row maxima, log2 units
   // row sums of the rounded P in lanes 0..15: query c of each block in l_lo,
   // query c + 16 in l_hi; EXACT_LSE: this lane's sums of the unrounded p
-  float l_lo[2] = {0.f, 0.f}, l_hi[2] = {0.f, 0.f}, l_ex[2] = {0.f, 0.f};
-  f32x16_t t0;                 // exponent arguments of the current sub-tile, query block 0
-  f32x16_t s1;                 // raw logits of the current sub-tile, query block 1
-  bf16x8_t pA[2][2], pB[2][2]; // P of two consecutive sub-tiles [query block][key half]
-  // LDS byte offsets of the ring slots the iteration of pipeline position u
-  // uses: K of positions u, u+1, u+3 and V of u, u+2. They rotate by one
-  // slot per iteration (scalar adds instead of a modulo per use).
-  struct Ring {
-    int k0, k1, k3, v0, v2;
-  };
-  Ring ring;
+  float l_lo[2], l_hi[2], l_ex[2];
 
-  // ---- prologue: K tiles u0..u0+2, V tiles u0, u0+1; the first sub-tile's
-  // logits and their exact row maxima. The first iteration reads K u0, K u0+1
-  // and V u0 only, so K u0+2 and V u0+1 go last and stay in flight (their 10
-  // instructions) until that iteration's own wait; the Q loads, issued before
-  // all of them, are complete once those are the only ones left.
-  dma_tile(Kh, ktile(u0), kslot(u0), kdo);
-  dma_tile(Vh, ktile(u0), vslot(u0), vdo);
-  if (u0 + 1 < u1) dma_tile(Kh, ktile(u0 + 1), kslot(u0 + 1), kdo);
-  if (u0 + 2 < u1) {
-    dma_tile(Kh, ktile(u0 + 2), kslot(u0 + 2), kdo);
-    dma_tile(Vh, ktile(u0 + 1), vslot(u0 + 1), vdo);
-    __builtin_amdgcn_s_waitcnt(0x0F7A);    // vmcnt(10)
-  } else {
-    if (u0 + 1 < u1) dma_tile(Vh, ktile(u0 + 1), vslot(u0 + 1), vdo);
-    __builtin_amdgcn_s_waitcnt(0x0F70);    // vmcnt(0)
-  }
-  __syncthreads();
-  read_kfrags(2 * u0);
-  {
-    f32x16_t s0;
-    s_chain(0, s0);
-    s_chain(1, s1);
-    if (ksub(2 * u0) + 32 > N) { mask_keys(2 * u0, s0); mask_keys(2 * u0, s1); }
-    mc[0] = row_max(s0);
-    mc[1] = row_max(s1);
+  // One pass over the tile's keys. CHECKED: the running maximum moves when
+  // a sub-tile's sums of 16 p pass 2^64 or are not finite (the rare path
+  // below). Not CHECKED: it stays at the first sub-tile's exact maximum, the
+  // row-sum products of a sub-tile go back to back into running sums that
+  // nothing reads in the loop, and the caller tests the final sums once; a
+  // tile whose sums are not all finite and at most 2^64 runs again CHECKED.
+  auto pass = [&](auto checked_c) __attribute__((always_inline)) {
+    constexpr bool CHECKED = decltype(checked_c)::value;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) t0[r] = fmaf(s0[r], scale_log2, -mc[0]);
-  }
-  read_kfrags(2 * u0 + 1);          // the K fragments a sub-iteration starts with are those of the next sub-tile
-  // the first phase X adds 0 * 0: no previous sub-tile yet
+    for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-  for (int h = 0; h < 2; ++h)
+      for (int db = 0; db < DB; ++db)
 #pragma unroll
-    for (int x = 0; x < 2; ++x) pA[h][x] = bf16x8_t{};
+        for (int r = 0; r < 16; ++r) acc[qb][db][r] = 0.f;
 #pragma unroll
-  for (int h = 0; h < 2; ++h)
-#pragma unroll
-    for (int db = 0; db < DB; ++db) vf[h][db] = bf16x8_t{};
+    for (int qb = 0; qb < 2; ++qb) l_lo[qb] = l_hi[qb] = l_ex[qb] = 0.f;
+    f32x4_t lrun[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};   // not CHECKED: running sums
+    f32x16_t t0;                 // exponent arguments of the current sub-tile, query block 0
+    f32x16_t s1;                 // raw logits of the current sub-tile, query block 1
+    bf16x8_t pA[2][2], pB[2][2]; // P of two consecutive sub-tiles [query block][key half]
+    // LDS byte offsets of the ring slots the iteration of pipeline position u
+    // uses: K of positions u, u+1, u+3 and V of u, u+2. They rotate by one
+    // slot per iteration (scalar adds instead of a modulo per use).
+    struct Ring {
+      int k0, k1, k3, v0, v2;
+    };
+    Ring ring;
 
-  // One sub-iteration j. On entry: P_{j-1} (pin), V_{j-1} fragments (vf),
-  // K_{j+1} fragments (kf), S_j's exponent arguments for query block 0 (t0)
-  // and raw logits for query block 1 (s1). Two phases of 8 steps; each step
-  // is one P V MFMA (independent accumulators) and one S_{j+1} MFMA (a chain),
-  // with half of the same VALU mix behind each: two exponentials of P_j with
-  // their row-sum adds and bf16 pack, and two FMAs. The LDS reads of the next
-  // fragments follow the MFMA that last reads the register: V_j during both
-  // phases, K_{j+2} during phase Y. On exit the state holds sub-tile j+1.
-  // MASK: keys of S_{j+1} (and, on the rare path, of S_j) may lie past N.
-  // dma(m) issues this sub-iteration's share of the tile DMA at phase-X step 2 m.
-  auto sub = [&](int j, bf16x8_t (&pin)[2][2], bf16x8_t (&pout)[2][2], auto mask_c, auto&& dma)
-      __attribute__((always_inline)) {
-    constexpr bool MASK = decltype(mask_c)::value;
-    float ls0 = 0.f, ls1 = 0.f;   // EXACT_LSE only
-    const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
-    f32x4_t rs0, rs1;          // matrix-core sums of P_j, query blocks 0 and 1
-    f32x16_t& t1 = s1;         // in place
-    f32x16_t sa, sb;           // S_{j+1} of query blocks 0 and 1
-    const char* vb = smem + ring.v0 + (j & 1) * 32 * VROW + v_rd;      // V of position j / 2
-    const char* kb2 = smem + ring.k1 + (j & 1) * 32 * KROW + k_rd;     // K of sub-tile j + 2
-    // ================= phase X: P_{j-1} V_{j-1} (keys 0-15), S_{j+1} block 0, P_j block 0
+    // ---- prologue: K tiles u0..u0+2, V tiles u0, u0+1; the first sub-tile's
+    // logits and their exact row maxima. The first iteration reads K u0, K u0+1
+    // and V u0 only, so K u0+2 and V u0+1 go last and stay in flight (their 10
+    // instructions) until that iteration's own wait; the Q loads, issued before
+    // all of them, are complete once those are the only ones left.
+    dma_tile(Kh, ktile(u0), kslot(u0), kdo);
+    dma_tile(Vh, ktile(u0), vslot(u0), vdo);
+    if (u0 + 1 < u1) dma_tile(Kh, ktile(u0 + 1), kslot(u0 + 1), kdo);
+    if (u0 + 2 < u1) {
+      dma_tile(Kh, ktile(u0 + 2), kslot(u0 + 2), kdo);
+      dma_tile(Vh, ktile(u0 + 1), vslot(u0 + 1), vdo);
+      __builtin_amdgcn_s_waitcnt(0x0F7A);    // vmcnt(10)
+    } else {
+      if (u0 + 1 < u1) dma_tile(Vh, ktile(u0 + 1), vslot(u0 + 1), vdo);
+      __builtin_amdgcn_s_waitcnt(0x0F70);    // vmcnt(0)
+    }
+    __syncthreads();
+    read_kfrags(2 * u0);
     {
-      const float m1 = mc[1];
-#pragma unroll
-      for (int st = 0; st < 8; ++st) {
-        const int qb = st & 1, db = st >> 1;
-        acc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[0][db], pin[qb][0], acc[qb][db], 0, 0, 0);
-        const float pa = exp_raw(t0, 2 * st), pb = exp_raw(t0, 2 * st + 1);
-        t1[2 * st] = fmaf(s1[2 * st], scale_log2, -m1);
-        t1[2 * st + 1] = fmaf(s1[2 * st + 1], scale_log2, -m1);
-        if ((st & 1) == 0) dma(st >> 1);
-        DIT_FENCE();
-        if (st == 0) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) sa[r] = 0.f;
+      f32x16_t s0;
+      s_chain(0, s0);
+      s_chain(1, s1);
+      if (ksub(2 * u0) + 32 > N) { mask_keys(2 * u0, s0); mask_keys(2 * u0, s1); }
+      mc[0] = row_max(s0);
+      mc[1] = row_max(s1);
+  #pragma unroll
+      for (int r = 0; r < 16; ++r) t0[r] = fmaf(s0[r], scale_log2, -mc[0]);
+    }
+    read_kfrags(2 * u0 + 1);          // the K fragments a sub-iteration starts with are those of the next sub-tile
+    // the first phase X adds 0 * 0: no previous sub-tile yet
+  #pragma unroll
+    for (int h = 0; h < 2; ++h)
+  #pragma unroll
+      for (int x = 0; x < 2; ++x) pA[h][x] = bf16x8_t{};
+  #pragma unroll
+    for (int h = 0; h < 2; ++h)
+  #pragma unroll
+      for (int db = 0; db < DB; ++db) vf[h][db] = bf16x8_t{};
+
+    // One sub-iteration j. On entry: P_{j-1} (pin), V_{j-1} fragments (vf),
+    // K_{j+1} fragments (kf), S_j's exponent arguments for query block 0 (t0)
+    // and raw logits for query block 1 (s1). Two phases of 8 steps; each step
+    // is one P V MFMA (independent accumulators) and one S_{j+1} MFMA (a chain),
+    // with half of the same VALU mix behind each: two exponentials of P_j with
+    // their row-sum adds and bf16 pack, and two FMAs. The LDS reads of the next
+    // fragments follow the MFMA that last reads the register: V_j during both
+    // phases, K_{j+2} during phase Y. On exit the state holds sub-tile j+1.
+    // MASK: keys of S_{j+1} (and, on the rare path, of S_j) may lie past N.
+    // dma(m) issues this sub-iteration's share of the tile DMA at phase-X step 2 m.
+    auto sub = [&](int j, bf16x8_t (&pin)[2][2], bf16x8_t (&pout)[2][2], auto mask_c, auto&& dma)
+        __attribute__((always_inline)) {
+      constexpr bool MASK = decltype(mask_c)::value;
+      float ls0 = 0.f, ls1 = 0.f;   // EXACT_LSE only
+      const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
+      f32x4_t rs0, rs1;          // matrix-core sums of P_j, query blocks 0 and 1
+      f32x16_t& t1 = s1;         // in place
+      f32x16_t sa, sb;           // S_{j+1} of query blocks 0 and 1
+      const char* vb = smem + ring.v0 + (j & 1) * 32 * VROW + v_rd;      // V of position j / 2
+      const char* kb2 = smem + ring.k1 + (j & 1) * 32 * KROW + k_rd;     // K of sub-tile j + 2
+      // ================= phase X: P_{j-1} V_{j-1} (keys 0-15), S_{j+1} block 0, P_j block 0
+      {
+        const float m1 = mc[1];
+  #pragma unroll
+        for (int st = 0; st < 8; ++st) {
+          const int qb = st & 1, db = st >> 1;
+          acc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[0][db], pin[qb][0], acc[qb][db], 0, 0, 0);
+          const float pa = exp_raw(t0, 2 * st), pb = exp_raw(t0, 2 * st + 1);
+          t1[2 * st] = fmaf(s1[2 * st], scale_log2, -m1);
+          t1[2 * st + 1] = fmaf(s1[2 * st + 1], scale_log2, -m1);
+          if ((st & 1) == 0) dma(st >> 1);
+          DIT_FENCE();
+          if (st == 0) {
+  #pragma unroll
+            for (int r = 0; r < 16; ++r) sa[r] = 0.f;
+          }
+          sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[st], qf[0][st], sa, 0, 0, 0);
+          if (CHECKED && st == 4) rs0 = psum(pout[0][0], zero4);   // words 0-3 were packed in steps 0-3
+          sum_pack(ls0, pa, pb, st, pout[0]);
+          if (st & 1) read_vfrag(vb, 0, db);      // both query blocks have used vf[0][db]
+          DIT_FENCE();
         }
-        sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[st], qf[0][st], sa, 0, 0, 0);
-        if (st == 4) rs0 = psum(pout[0][0], zero4);   // words 0-3 were packed in steps 0-3
-        sum_pack(ls0, pa, pb, st, pout[0]);
-        if (st & 1) read_vfrag(vb, 0, db);      // both query blocks have used vf[0][db]
-        DIT_FENCE();
       }
-    }
-    if constexpr (MASK) {
-      if (ksub(j + 1) + 32 > N) mask_keys(j + 1, sa);
-    }
-    // ================= phase Y: P_{j-1} V_{j-1} (keys 16-31), S_{j+1} block 1, P_j block 1
+      if constexpr (MASK) {
+        if (ksub(j + 1) + 32 > N) mask_keys(j + 1, sa);
+      }
+      // ================= phase Y: P_{j-1} V_{j-1} (keys 16-31), S_{j+1} block 1, P_j block 1
+      {
+        const float m0 = mc[0];
+  #pragma unroll
+        for (int st = 0; st < 8; ++st) {
+          const int qb = st & 1, db = st >> 1;
+          acc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[1][db], pin[qb][1], acc[qb][db], 0, 0, 0);
+          const float pa = exp_raw(t1, 2 * st), pb = exp_raw(t1, 2 * st + 1);
+          t0[2 * st] = fmaf(sa[2 * st], scale_log2, -m0);        // S_{j+1}'s arguments
+          t0[2 * st + 1] = fmaf(sa[2 * st + 1], scale_log2, -m0);
+          DIT_FENCE();
+          if (st == 0) {
+  #pragma unroll
+            for (int r = 0; r < 16; ++r) sb[r] = 0.f;
+          }
+          sb = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[st], qf[1][st], sb, 0, 0, 0);
+          if (CHECKED && st == 0) rs0 = psum(pout[0][1], rs0);
+          if (CHECKED && st == 4) rs1 = psum(pout[1][0], zero4);
+          sum_pack(ls1, pa, pb, st, pout[1]);
+          read_kfrag(kb2, st);                     // kf[st] is free: K_{j+2}
+          if (st & 1) read_vfrag(vb, 1, db);
+          DIT_FENCE();
+        }
+      }
+      if constexpr (MASK) {
+        if (ksub(j + 1) + 32 > N) mask_keys(j + 1, sb);
+      }
+      s1 = sb;
+      // The packed P must exist here: without this the compiler sinks the bf16
+      // packs past the rare-path branch, out of the MFMA phases.
+      asm volatile("" ::"v"(pout[0][0]), "v"(pout[0][1]), "v"(pout[1][0]), "v"(pout[1][1]));
+      if constexpr (CHECKED) {
+        rs1 = psum(pout[1][1], rs1);
+        // ---- rare path: a sum of 16 of sub-tile j's p passed 2^64 or is not
+        // finite. The sums are >= +0 or NaN, so their bit patterns order like the
+        // values, with every NaN above +inf: one unsigned maximum decides.
+        auto bits = [](float x) { return __float_as_uint(x); };
+        const uint32_t big = max(max(max(bits(rs0[0]), bits(rs0[1])), max(bits(rs0[2]), bits(rs0[3]))),
+                                 max(max(bits(rs1[0]), bits(rs1[1])), max(bits(rs1[2]), bits(rs1[3]))));
+        if (__builtin_expect(__builtin_amdgcn_ballot_w64(big > __float_as_uint(kPipeSumLimit)) != 0, 0)) {
+          read_kfrags_at(smem + ring.k0 + (j & 1) * 32 * KROW + k_rd);   // K tiles j/2 and (j+2)/2 are still in their slots
+    #pragma unroll
+          for (int qb = 0; qb < 2; ++qb) {
+            f32x16_t s;
+            s_chain(qb, s);
+            if constexpr (MASK) {
+              if (ksub(j) + 32 > N) mask_keys(j, s);
+            }
+            const float m_new = fmaxf(mc[qb], row_max(s));
+            const float alpha = fast_exp2(mc[qb] - m_new);
+            l_lo[qb] *= __shfl(alpha, lane & 15);
+            l_hi[qb] *= __shfl(alpha, (lane & 15) + 16);
+            if constexpr (EXACT_LSE) l_ex[qb] *= alpha;
+    #pragma unroll
+            for (int db = 0; db < DB; ++db)
+    #pragma unroll
+              for (int r = 0; r < 16; ++r) acc[qb][db][r] *= alpha;
+            if (qb == 0) {
+              const float shift = m_new - mc[0];
+    #pragma unroll
+              for (int r = 0; r < 16; ++r) t0[r] -= shift;    // S_{j+1}'s arguments used the old maximum
+            }
+            mc[qb] = m_new;
+    #pragma unroll
+            for (int r = 0; r < 16; ++r) s[r] = fmaf(s[r], scale_log2, -m_new);
+            float& ls = qb == 0 ? ls0 : ls1;
+            ls = 0.f;
+    #pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const float pa = exp_one(s, 2 * e, ls);
+              pack_word(pa, exp_one(s, 2 * e + 1, ls), e, pout[qb]);
+            }
+          }
+          rs0 = psum(pout[0][1], psum(pout[0][0], zero4));
+          rs1 = psum(pout[1][1], psum(pout[1][0], zero4));
+          read_kfrags_at(kb2);
+        }
+        l_lo[0] += rs0[0] + rs0[2];
+        l_hi[0] += rs0[1] + rs0[3];
+        l_lo[1] += rs1[0] + rs1[2];
+        l_hi[1] += rs1[1] + rs1[3];
+      } else {
+        // the four row-sum products of P_j back to back, into the running sums
+        lrun[0] = psum(pout[0][0], lrun[0]);
+        lrun[1] = psum(pout[1][0], lrun[1]);
+        lrun[0] = psum(pout[0][1], lrun[0]);
+        lrun[1] = psum(pout[1][1], lrun[1]);
+        (void)rs0;
+        (void)rs1;
+      }
+      if constexpr (EXACT_LSE) {
+        l_ex[0] += ls0;
+        l_ex[1] += ls1;
+      }
+    };
+
     {
-      const float m0 = mc[0];
-#pragma unroll
-      for (int st = 0; st < 8; ++st) {
-        const int qb = st & 1, db = st >> 1;
-        acc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[1][db], pin[qb][1], acc[qb][db], 0, 0, 0);
-        const float pa = exp_raw(t1, 2 * st), pb = exp_raw(t1, 2 * st + 1);
-        t0[2 * st] = fmaf(sa[2 * st], scale_log2, -m0);        // S_{j+1}'s arguments
-        t0[2 * st + 1] = fmaf(sa[2 * st + 1], scale_log2, -m0);
-        DIT_FENCE();
-        if (st == 0) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) sb[r] = 0.f;
+      auto rfl = [](int x) { return __builtin_amdgcn_readfirstlane(x); };
+      ring.k0 = rfl((u0 % C::kKSlots) * C::kSlot);
+      ring.k1 = rfl(((u0 + 1) % C::kKSlots) * C::kSlot);
+      ring.k3 = rfl(((u0 + 3) % C::kKSlots) * C::kSlot);
+      ring.v0 = rfl(C::kVBase + (u0 % C::kVSlots) * C::kSlot);
+      ring.v2 = rfl(C::kVBase + ((u0 + 2) % C::kVSlots) * C::kSlot);
+    }
+    auto advance_ring = [&]() __attribute__((always_inline)) {
+      ring.k3 = ring.k0;
+      ring.k0 = ring.k1;
+      ring.k1 = ring.k1 == (C::kKSlots - 1) * C::kSlot ? 0 : ring.k1 + C::kSlot;
+      ring.v2 = ring.v0;
+      ring.v0 = ring.v0 == C::kVBase + (C::kVSlots - 1) * C::kSlot ? C::kVBase : ring.v0 + C::kSlot;
+    };
+
+    // One 64-key tile u. It streams in K tile u+3 (during its first
+    // sub-iteration) and V tile u+2 (during its second), one DMA instruction on
+    // every other phase-X step, and then waits for the tiles issued one iteration earlier
+    // (K u+2, V u+1) before the barrier that publishes them. In the steady
+    // state (TAIL false) both DMAs exist and no key of tiles u, u+1 lies past N,
+    // so the body has no branch but the rare path: a branch would let the
+    // compiler sink the softmax work out of the MFMA phases.
+    // rk, rv: the descriptors of the key tiles at positions u + 3 (K) and u + 2
+    // (V); before_wait() runs after the compute, ahead of the wait for the
+    // tiles (the next iteration's scalar bookkeeping goes there, behind the
+    // last MFMAs in flight).
+    auto iteration = [&](int u, auto tail_c, const i32x4_t& rk, const i32x4_t& rv, auto&& before_wait)
+        __attribute__((always_inline)) {
+      constexpr bool TAIL = decltype(tail_c)::value;
+      const bool k_next = !TAIL || u + 3 < u1, v_next = !TAIL || u + 2 < u1;
+      const char* sk = smem + ring.k3;
+      const char* sv = smem + ring.v2;
+      DIT_FENCE();
+      // hook steps st = 0..3 issue instructions m = st, and m = 4 at st = 0
+      static_assert(C::kDmaPerWave == 5, "DMA hook spreads 5 instructions over 4 steps");
+      sub(2 * u, pA, pB, tail_c, [&](int st) __attribute__((always_inline)) {
+        if (k_next) {
+          dma_one(rk, sk, kdo, st);
+          if (st == 0) dma_one(rk, sk, kdo, 4);
         }
-        sb = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[st], qf[1][st], sb, 0, 0, 0);
-        if (st == 0) rs0 = psum(pout[0][1], rs0);
-        if (st == 4) rs1 = psum(pout[1][0], zero4);
-        sum_pack(ls1, pa, pb, st, pout[1]);
-        read_kfrag(kb2, st);                     // kf[st] is free: K_{j+2}
-        if (st & 1) read_vfrag(vb, 1, db);
-        DIT_FENCE();
+      });
+      sub(2 * u + 1, pB, pA, tail_c, [&](int st) __attribute__((always_inline)) {
+        if (v_next) {
+          dma_one(rv, sv, vdo, st);
+          if (st == 0) dma_one(rv, sv, vdo, 4);
+        }
+      });
+      DIT_FENCE();
+      before_wait();
+      advance_ring();
+      if (TAIL)
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+      else
+        __builtin_amdgcn_s_waitcnt(0x0F7A);  // vmcnt(10): this iteration's 10 DMAs may stay in flight
+      __syncthreads();
+      DIT_FENCE();
+    };
+    // Sub-tiles past u1 that the pipeline touches (S of sub-tile 2 u1) read a
+    // slot that is stale or zero: their values are never used.
+    int u = u0;
+    if constexpr (SPARSE) {
+      // A steady-state iteration loads the next one's K tile index while it
+      // waits for its DMAs (a scalar load waited for at the top of the loop
+      // would stall every wave there).
+      int tk = ktile(u0 + 3), tv = ktile(u0 + 2);
+      for (; u + 3 < u1; ++u) {
+        int tk_next;
+        iteration(u, flag_t<false>{}, tile_rsrc(Kh, tk), tile_rsrc(Vh, tv), [&] {
+          tk_next = ktile(u + 4);
+          asm volatile("" : "+s"(tk_next));
+        });
+        tv = tk;
+        tk = tk_next;
       }
+      for (; u < u1; ++u) iteration(u, flag_t<true>{}, tile_rsrc(Kh, ktile(u + 3)), tile_rsrc(Vh, ktile(u + 2)), [] {});
+    } else {
+      // the tiles at positions u + 3 (K) and u + 2 (V): addresses and rows left,
+      // advanced by one tile per iteration
+      const unsigned long long tile_bytes = (unsigned long long)64 * rowb;
+      unsigned long long ka = (unsigned long long)(Kh + (long long)(u0 + 3) * 64 * rowb);
+      unsigned long long va = (unsigned long long)(Vh + (long long)(u0 + 2) * 64 * rowb);
+      int kr = N - (u0 + 3) * 64, vr = N - (u0 + 2) * 64;
+      auto advance = [&]() __attribute__((always_inline)) {
+        ka += tile_bytes;
+        va += tile_bytes;
+        kr -= 64;
+        vr -= 64;
+      };
+      for (; u + 3 < u1; ++u) iteration(u, flag_t<false>{}, make_rsrc(ka, kr), make_rsrc(va, vr), advance);
+      for (; u < u1; ++u) iteration(u, flag_t<true>{}, make_rsrc(ka, kr), make_rsrc(va, vr), advance);
     }
-    if constexpr (MASK) {
-      if (ksub(j + 1) + 32 > N) mask_keys(j + 1, sb);
-    }
-    s1 = sb;
-    // The packed P must exist here: without this the compiler sinks the bf16
-    // packs past the rare-path branch, out of the MFMA phases.
-    asm volatile("" ::"v"(pout[0][0]), "v"(pout[0][1]), "v"(pout[1][0]), "v"(pout[1][1]));
-    rs1 = psum(pout[1][1], rs1);
-    // ---- rare path: a sum of 16 of sub-tile j's p passed 2^64 or is not
-    // finite. The sums are >= +0 or NaN, so their bit patterns order like the
-    // values, with every NaN above +inf: one unsigned maximum decides.
-    auto bits = [](float x) { return __float_as_uint(x); };
-    const uint32_t big = max(max(max(bits(rs0[0]), bits(rs0[1])), max(bits(rs0[2]), bits(rs0[3]))),
-                             max(max(bits(rs1[0]), bits(rs1[1])), max(bits(rs1[2]), bits(rs1[3]))));
-    if (__builtin_expect(__builtin_amdgcn_ballot_w64(big > __float_as_uint(kPipeSumLimit)) != 0, 0)) {
-      read_kfrags_at(smem + ring.k0 + (j & 1) * 32 * KROW + k_rd);   // K tiles j/2 and (j+2)/2 are still in their slots
+
+    // ---- P V of the last sub-tile (its V fragments were read in the last phase Y)
+  #pragma unroll
+    for (int half = 0; half < 2; ++half)
+  #pragma unroll
+      for (int db = 0; db < DB; ++db)
+  #pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+          acc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[half][db], pA[qb][half], acc[qb][db], 0, 0, 0);
+    if constexpr (!CHECKED) {
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
-        f32x16_t s;
-        s_chain(qb, s);
-        if constexpr (MASK) {
-          if (ksub(j) + 32 > N) mask_keys(j, s);
-        }
-        const float m_new = fmaxf(mc[qb], row_max(s));
-        const float alpha = fast_exp2(mc[qb] - m_new);
-        l_lo[qb] *= __shfl(alpha, lane & 15);
-        l_hi[qb] *= __shfl(alpha, (lane & 15) + 16);
-        if constexpr (EXACT_LSE) l_ex[qb] *= alpha;
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc[qb][db][r] *= alpha;
-        if (qb == 0) {
-          const float shift = m_new - mc[0];
-#pragma unroll
-          for (int r = 0; r < 16; ++r) t0[r] -= shift;    // S_{j+1}'s arguments used the old maximum
-        }
-        mc[qb] = m_new;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[r] = fmaf(s[r], scale_log2, -m_new);
-        float& ls = qb == 0 ? ls0 : ls1;
-        ls = 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float pa = exp_one(s, 2 * e, ls);
-          pack_word(pa, exp_one(s, 2 * e + 1, ls), e, pout[qb]);
-        }
+        l_lo[qb] = lrun[qb][0] + lrun[qb][2];
+        l_hi[qb] = lrun[qb][1] + lrun[qb][3];
       }
-      rs0 = psum(pout[0][1], psum(pout[0][0], zero4));
-      rs1 = psum(pout[1][1], psum(pout[1][0], zero4));
-      read_kfrags_at(kb2);
-    }
-    l_lo[0] += rs0[0] + rs0[2];
-    l_hi[0] += rs0[1] + rs0[3];
-    l_lo[1] += rs1[0] + rs1[2];
-    l_hi[1] += rs1[1] + rs1[3];
-    if constexpr (EXACT_LSE) {
-      l_ex[0] += ls0;
-      l_ex[1] += ls1;
     }
   };
-
+  pass(flag_t<false>{});
   {
-    auto rfl = [](int x) { return __builtin_amdgcn_readfirstlane(x); };
-    ring.k0 = rfl((u0 % C::kKSlots) * C::kSlot);
-    ring.k1 = rfl(((u0 + 1) % C::kKSlots) * C::kSlot);
-    ring.k3 = rfl(((u0 + 3) % C::kKSlots) * C::kSlot);
-    ring.v0 = rfl(C::kVBase + (u0 % C::kVSlots) * C::kSlot);
-    ring.v2 = rfl(C::kVBase + ((u0 + 2) % C::kVSlots) * C::kSlot);
-  }
-  auto advance_ring = [&]() __attribute__((always_inline)) {
-    ring.k3 = ring.k0;
-    ring.k0 = ring.k1;
-    ring.k1 = ring.k1 == (C::kKSlots - 1) * C::kSlot ? 0 : ring.k1 + C::kSlot;
-    ring.v2 = ring.v0;
-    ring.v0 = ring.v0 == C::kVBase + (C::kVSlots - 1) * C::kSlot ? C::kVBase : ring.v0 + C::kSlot;
-  };
-
-  // One 64-key tile u. It streams in K tile u+3 (during its first
-  // sub-iteration) and V tile u+2 (during its second), one DMA instruction on
-  // every other phase-X step, and then waits for the tiles issued one iteration earlier
-  // (K u+2, V u+1) before the barrier that publishes them. In the steady
-  // state (TAIL false) both DMAs exist and no key of tiles u, u+1 lies past N,
-  // so the body has no branch but the rare path: a branch would let the
-  // compiler sink the softmax work out of the MFMA phases.
-  // rk, rv: the descriptors of the key tiles at positions u + 3 (K) and u + 2
-  // (V); before_wait() runs after the compute, ahead of the wait for the
-  // tiles (the next iteration's scalar bookkeeping goes there, behind the
-  // last MFMAs in flight).
-  auto iteration = [&](int u, auto tail_c, const i32x4_t& rk, const i32x4_t& rv, auto&& before_wait)
-      __attribute__((always_inline)) {
-    constexpr bool TAIL = decltype(tail_c)::value;
-    const bool k_next = !TAIL || u + 3 < u1, v_next = !TAIL || u + 2 < u1;
-    const char* sk = smem + ring.k3;
-    const char* sv = smem + ring.v2;
-    DIT_FENCE();
-    // hook steps st = 0..3 issue instructions m = st, and m = 4 at st = 0
-    static_assert(C::kDmaPerWave == 5, "DMA hook spreads 5 instructions over 4 steps");
-    sub(2 * u, pA, pB, tail_c, [&](int st) __attribute__((always_inline)) {
-      if (k_next) {
-        dma_one(rk, sk, kdo, st);
-        if (st == 0) dma_one(rk, sk, kdo, 4);
-      }
-    });
-    sub(2 * u + 1, pB, pA, tail_c, [&](int st) __attribute__((always_inline)) {
-      if (v_next) {
-        dma_one(rv, sv, vdo, st);
-        if (st == 0) dma_one(rv, sv, vdo, 4);
-      }
-    });
-    DIT_FENCE();
-    before_wait();
-    advance_ring();
-    if (TAIL)
-      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-    else
-      __builtin_amdgcn_s_waitcnt(0x0F7A);  // vmcnt(10): this iteration's 10 DMAs may stay in flight
+    // the workgroup runs the tile again, checked, if a wave's sums overflowed
+    // (every lane: those of lanes 16..63 are zero); NaN fails the test
+    bool ok = l_lo[0] <= kPipeSumLimit && l_hi[0] <= kPipeSumLimit && l_lo[1] <= kPipeSumLimit &&
+              l_hi[1] <= kPipeSumLimit;
+    if constexpr (EXACT_LSE) ok = ok && l_ex[0] <= kPipeSumLimit && l_ex[1] <= kPipeSumLimit;
+    int* flags = reinterpret_cast<int*>(smem + C::kFlagOff);
+    if (lane == 0) flags[wave] = __builtin_amdgcn_ballot_w64(!ok) != 0 ? 1 : 0;
     __syncthreads();
-    DIT_FENCE();
-  };
-  // Sub-tiles past u1 that the pipeline touches (S of sub-tile 2 u1) read a
-  // slot that is stale or zero: their values are never used.
-  int u = u0;
-  if constexpr (SPARSE) {
-    // A steady-state iteration loads the next one's K tile index while it
-    // waits for its DMAs (a scalar load waited for at the top of the loop
-    // would stall every wave there).
-    int tk = ktile(u0 + 3), tv = ktile(u0 + 2);
-    for (; u + 3 < u1; ++u) {
-      int tk_next;
-      iteration(u, flag_t<false>{}, tile_rsrc(Kh, tk), tile_rsrc(Vh, tv), [&] {
-        tk_next = ktile(u + 4);
-        asm volatile("" : "+s"(tk_next));
-      });
-      tv = tk;
-      tk = tk_next;
-    }
-    for (; u < u1; ++u) iteration(u, flag_t<true>{}, tile_rsrc(Kh, ktile(u + 3)), tile_rsrc(Vh, ktile(u + 2)), [] {});
-  } else {
-    // the tiles at positions u + 3 (K) and u + 2 (V): addresses and rows left,
-    // advanced by one tile per iteration
-    const unsigned long long tile_bytes = (unsigned long long)64 * rowb;
-    unsigned long long ka = (unsigned long long)(Kh + (long long)(u0 + 3) * 64 * rowb);
-    unsigned long long va = (unsigned long long)(Vh + (long long)(u0 + 2) * 64 * rowb);
-    int kr = N - (u0 + 3) * 64, vr = N - (u0 + 2) * 64;
-    auto advance = [&]() __attribute__((always_inline)) {
-      ka += tile_bytes;
-      va += tile_bytes;
-      kr -= 64;
-      vr -= 64;
-    };
-    for (; u + 3 < u1; ++u) iteration(u, flag_t<false>{}, make_rsrc(ka, kr), make_rsrc(va, vr), advance);
-    for (; u < u1; ++u) iteration(u, flag_t<true>{}, make_rsrc(ka, kr), make_rsrc(va, vr), advance);
+    if ((flags[0] | flags[1] | flags[2] | flags[3]) != 0) pass(flag_t<true>{});
   }
-
-  // ---- P V of the last sub-tile (its V fragments were read in the last phase Y)
-#pragma unroll
-  for (int half = 0; half < 2; ++half)
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
-        acc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[half][db], pA[qb][half], acc[qb][db], 0, 0, 0);
 
   // The results go to memory through LDS. In the MFMA layout a lane holds
   // pieces of 32 different rows, so a direct store instruction touches 32 rows
