@@ -704,7 +704,9 @@ __device__ __forceinline__ void pipe_tile(const uint16_t* __restrict__ Qg, const
               l_hi[1] <= kPipeSumLimit;
     if constexpr (EXACT_LSE) ok = ok && l_ex[0] <= kPipeSumLimit && l_ex[1] <= kPipeSumLimit;
     int* flags = reinterpret_cast<int*>(smem + C::kFlagOff);
-    if (lane == 0) flags[wave] = __builtin_amdgcn_ballot_w64(!ok) != 0 ? 1 : 0;
+    // every lane votes: a ballot inside the lane-0 branch would see lane 0 only
+    const int overflowed = __builtin_amdgcn_ballot_w64(!ok) != 0 ? 1 : 0;
+    if (lane == 0) flags[wave] = overflowed;
     __syncthreads();
     if ((flags[0] | flags[1] | flags[2] | flags[3]) != 0) pass(flag_t<true>{});
   }

@@ -67,14 +67,17 @@ def say(*a):
     sys.stdout.flush()
 
 
-def gpu_attention(q, k, v, scale, want_lse=False):
-    """q, k, v: CPU tensors (bf16 or float8_e4m3fn). Returns (O float64 numpy, lse or None)."""
+def gpu_attention(q, k, v, scale, want_lse=False, workspace=None):
+    """q, k, v: CPU tensors (bf16 or float8_e4m3fn). Returns (O float64 numpy,
+    lse or None). workspace: None (the library's fastest schedule) or a number
+    of bytes of device workspace to hand over (0: one workgroup per tile)."""
     import diffusion_transformer_attention_non_amd as dit
     dev = torch.device("cuda:0")
     qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
     B, H, N, d = q.shape
     lse = torch.empty((B, H, N), dtype=torch.float32, device=dev) if want_lse else None
-    o = dit.attention(qd, kd, vd, scale, lse=lse)
+    ws = None if workspace is None else torch.empty(workspace, dtype=torch.uint8, device=dev)
+    o = dit.attention(qd, kd, vd, scale, lse=lse, workspace=ws)
     torch.cuda.synchronize()
     return o.float().cpu().double().numpy(), (lse.cpu().double().numpy() if want_lse else None)
 

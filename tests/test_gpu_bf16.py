@@ -13,9 +13,9 @@ from workloads import (WORKLOADS, coverage_pattern, constant_values, dominating_
 pytestmark = pytest.mark.gpu
 
 
-def _full_check(q, k, v, scale, label, lse=True):
+def _full_check(q, k, v, scale, label, lse=True, workspace=None):
     say(f"[gpu] {label}: shape {tuple(q.shape)}")
-    o, l = gpu_attention(q, k, v, scale, want_lse=lse)
+    o, l = gpu_attention(q, k, v, scale, want_lse=lse, workspace=workspace)
     check_full(o, l, q, k, scale, oracle_ref(q, k, v, scale), label)
     return o
 
@@ -176,3 +176,35 @@ def test_growing_logits(slope, label):
     the first sub-tile's maximum reach about 2^50 and are used as they are."""
     q, k, v = _ramp_qkv(1000, 128, slope, seed=31)
     _full_check(q, k, v, 1 / math.sqrt(128), f"ramp slope {slope} ({label})")
+
+
+@pytest.mark.parametrize("schedule,H,N,q_700,lse", [("split", 2, 1000, 100.0, True), ("split", 2, 1000, 100.0, False),
+                                                     ("tile", 2, 1000, 45.0, True), ("tile", 2, 1000, 100.0, False),
+                                                     ("streamk", 3, 4096, 100.0, True)])
+def test_one_row_overflow_reruns_its_workgroup(schedule, H, N, q_700, lse):
+    """One query row (row 700: lane 12 of the third wave of the third 256-row
+    tile, a row that lane 0 does not hold) has logits that grow by 0.0044 q_700
+    nats per key; the other rows grow about 50 times more slowly. The unchecked
+    first pass of a range of keys in which that row's growth passes 64 bits
+    overflows (a p past 2^128 also makes the row sums of its 16-row group
+    NaN), and only in that wave, so the whole workgroup must run the range
+    again checked. The split schedule of B=1 H=2 N=1000 gives a workgroup 4 key
+    tiles (about 163 bits of growth at q_700 = 100); without workspace a
+    workgroup takes all 1000 keys (287 bits at q_700 = 45); stream-K at B=1
+    H=3 N=4096 gives each workgroup 12 key tiles, cut across tile boundaries,
+    so a workgroup may run two ranges back to back. Every row must match the
+    oracle."""
+    import diffusion_transformer_attention_non_amd as dit
+    d = 128
+    want = {"tile": dit.DIT_ATTN_SCHED_TILE, "split": dit.DIT_ATTN_SCHED_SPLIT,
+            "streamk": dit.DIT_ATTN_SCHED_STREAMK}[schedule]
+    ws_bytes = dit.workspace_bytes(1, H, N, d, lse=lse) if schedule != "tile" else 0
+    st, plan = dit.dit_attn_plan(1, H, N, d, dit.DIT_ATTN_BF16, 0, lse, 0, ws_bytes)
+    assert st == 0 and plan.schedule == want, (plan.schedule, want)
+    q, k, v = random_qkv(1, H, N, d, seed=41)
+    q, k = q.float(), k.float()
+    k[..., 0] = 0.05 * torch.arange(N, dtype=torch.float32)
+    q[:, :, 700, 0] = q_700
+    q, k = q.bfloat16(), k.bfloat16()
+    _full_check(q, k, v, 1 / math.sqrt(d), f"one overflowing row (row 700, q {q_700}, {schedule}, H={H} N={N})",
+                lse=lse, workspace=ws_bytes if schedule != "tile" else 0)
