@@ -8,7 +8,7 @@ import torch
 import oracle
 from parity import check_bf16, check_full, gpu_attention, logit_scale, oracle_ref, oracle_workload, say
 from workloads import (WORKLOADS, coverage_pattern, constant_values, dominating_key, identical_keys,
-                       make_qkv, random_qkv)
+                       make_qkv, one_growing_row, random_qkv)
 
 pytestmark = pytest.mark.gpu
 
@@ -201,10 +201,15 @@ def test_one_row_overflow_reruns_its_workgroup(schedule, H, N, q_700, lse):
     ws_bytes = dit.workspace_bytes(1, H, N, d, lse=lse) if schedule != "tile" else 0
     st, plan = dit.dit_attn_plan(1, H, N, d, dit.DIT_ATTN_BF16, 0, lse, 0, ws_bytes)
     assert st == 0 and plan.schedule == want, (plan.schedule, want)
-    q, k, v = random_qkv(1, H, N, d, seed=41)
-    q, k = q.float(), k.float()
-    k[..., 0] = 0.05 * torch.arange(N, dtype=torch.float32)
-    q[:, :, 700, 0] = q_700
-    q, k = q.bfloat16(), k.bfloat16()
+    q, k, v = one_growing_row(1, H, N, d, q_row=q_700)
     _full_check(q, k, v, 1 / math.sqrt(d), f"one overflowing row (row 700, q {q_700}, {schedule}, H={H} N={N})",
                 lse=lse, workspace=ws_bytes if schedule != "tile" else 0)
+
+
+def test_one_row_overflow_d64():
+    """The d = 64 kernel with one row whose logits grow about 0.64 bits per
+    key (row 700, not a lane-0 row) while the others stay near the first
+    sub-tile's maximum."""
+    N, d = 1000, 64
+    q, k, v = one_growing_row(1, 2, N, d, q_row=100.0 * math.sqrt(64 / 128))
+    _full_check(q, k, v, 1 / math.sqrt(d), "d=64 one overflowing row (row 700)")

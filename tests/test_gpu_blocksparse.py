@@ -14,7 +14,7 @@ import torch
 
 import oracle
 from parity import check_bf16, lse_tolerance, logit_scale, say
-from workloads import make_qkv, random_kv_blocks, random_qkv, sample_rows
+from workloads import make_qkv, one_growing_row, random_kv_blocks, random_qkv, sample_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -75,6 +75,19 @@ def test_blocksparse_matches_oracle(B, H, N, density, empty_every, seed):
     say(f"[gpu] blocksparse B={B} H={H} N={N} density={density} empty_every={empty_every} "
         f"max_blocks={blocks.shape[-1]}")
     _compare(q, k, v, blocks, counts, 1 / math.sqrt(d), f"sparse N={N}")
+
+
+@pytest.mark.parametrize("density", [0.6, 1.0])
+def test_blocksparse_one_row_overflow(density):
+    """One row (row 700, lane 12 of its wave) whose logits grow far faster
+    along the keys than the others': its unchecked first pass over a tile's
+    listed key blocks overflows in one wave, and the workgroup must run the
+    tile again checked."""
+    d = 128
+    q, k, v = one_growing_row(1, 2, 1000, d)
+    blocks, counts = random_kv_blocks(1, 2, 1000, density, seed=7)
+    say(f"[gpu] blocksparse one growing row, density {density}")
+    _compare(q, k, v, blocks, counts, 1 / math.sqrt(d), f"sparse one growing row density={density}")
 
 
 def test_blocksparse_hand_lists():

@@ -13,7 +13,7 @@ import torch
 
 import oracle
 from parity import SPEC_MAX_FP8, check_fp8_against_emulation, fp8_bound, lse_tolerance, say
-from workloads import block_varied_qkv, make_qkv, random_qkv, sample_rows
+from workloads import block_varied_qkv, make_qkv, one_growing_row, random_qkv, sample_rows
 
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
@@ -129,6 +129,14 @@ def test_mx_attention_small(N):
 def test_mx_attention_block_varied(N):
     q, k, v = block_varied_qkv(1, 2, N, 128, seed=600 + N)
     _check_mx(q, k, v, 1 / math.sqrt(128), f"block-varied N={N}")
+
+
+def test_mx_one_row_overflow():
+    """One row (row 700, lane 12 of its wave) whose logits grow about 40 bits
+    per 64-key sub-tile; the block-scaled form's recompute must serve that
+    wave alone. Against the MX emulation."""
+    q, k, v = one_growing_row(1, 2, 1000, 128)
+    _check_mx(q, k, v, 1 / math.sqrt(128), "one growing row")
 
 
 def test_mx_attention_t2i_2048_sampled_rows():

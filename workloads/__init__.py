@@ -114,6 +114,19 @@ def random_qkv(B, H, N, d, seed=0, std=1.0):
     return tuple(out)
 
 
+def one_growing_row(B, H, N, d, row=700, q_row=100.0, slope=0.05, seed=41):
+    """iid N(0, 1) bf16 tensors in which one query row's logits grow along
+    the keys: K's first feature is slope * j for key j and Q's first feature
+    is q_row in that row, so its logits rise by slope * q_row / sqrt(d) per
+    key (the other rows, whose first feature is N(0, 1), about 50 times
+    more slowly at q_row = 100)."""
+    q, k, v = random_qkv(B, H, N, d, seed=seed)
+    q, k = q.float(), k.float()
+    k[..., 0] = slope * torch.arange(N, dtype=torch.float32)
+    q[:, :, row, 0] = q_row
+    return q.to(torch.bfloat16), k.to(torch.bfloat16), v
+
+
 def sample_rows(N: int, seed: int, n_edge: int = 256, stride: int = 16) -> np.ndarray:
     """Sorted query-row indices: every row of the first and last ``n_edge``
     rows plus a seeded 1/``stride`` sample of the rest. Used to compare large
