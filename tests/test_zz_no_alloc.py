@@ -11,7 +11,7 @@ import torch
 
 import oracle
 from parity import check_full, oracle_ref, say
-from workloads import random_qkv, sample_rows
+from workloads import one_growing_row, random_qkv, sample_rows
 
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
@@ -81,6 +81,22 @@ def test_noalloc_fp8_then_smaller_bf16():
     assert torch.equal(o_na, o_ws) and torch.equal(l_na, l_ws)
     check_full(o_na.float().cpu().double().numpy(), l_na.cpu().double().numpy(), q, k, 1 / math.sqrt(128),
                oracle_ref(q, k, v, 1 / math.sqrt(128)), "noalloc B=1 H=2 N=3000")
+
+
+def test_noalloc_one_growing_row_reruns_like_the_workspace_form():
+    """One row whose logits outgrow the unchecked first pass (row 700, not a
+    lane-0 row): the workgroup's checked rerun under the static scratch, at
+    a stream-K shape and then a smaller split shape, bit for bit the
+    workspace form's result and every row within the bound of the oracle."""
+    for B, H, N in [(1, 3, 4096), (1, 2, 1000)]:
+        d = 128
+        q, k, v = one_growing_row(B, H, N, d)
+        scale = 1 / math.sqrt(d)
+        say(f"[gpu] noalloc one growing row: B={B} H={H} N={N}")
+        (o_na, l_na), (o_ws, l_ws) = _both(q.to(DEV), k.to(DEV), v.to(DEV), scale)
+        assert torch.equal(o_na, o_ws) and torch.equal(l_na, l_ws), (B, H, N)
+        check_full(o_na.float().cpu().double().numpy(), l_na.cpu().double().numpy(), q, k, scale,
+                   oracle_ref(q, k, v, scale), f"noalloc one growing row B={B} H={H} N={N}")
 
 
 def test_noalloc_rejects_bad_arguments_before_launch():
