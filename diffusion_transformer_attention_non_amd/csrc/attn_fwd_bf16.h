@@ -79,7 +79,7 @@ void attn_fwd_bf16_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __res
                           const uint16_t* __restrict__ Vg, uint16_t* __restrict__ Og,
                           float* __restrict__ LSEg, int N, int n_qtiles,
                           float scale_log2, float scale, Layout L) {
-  constexpr int D = C::kD, QB = C::kQB, KB = C::kKB, KS = C::kKS, DB = C::kDB, KBLK = C::kKBLK;
+  constexpr int QB = C::kQB, KB = C::kKB, KS = C::kKS, DB = C::kDB, KBLK = C::kKBLK;
   constexpr int CH = C::kChunks, TB = C::kTileBytes;
   extern __shared__ __attribute__((aligned(16))) char smem[];
 

@@ -296,7 +296,6 @@ __device__ __forceinline__ void pipe_tile(const uint16_t* __restrict__ Qg, const
   };
   auto read_kfrags = [&](int j) { read_kfrags_at(kbase(j)); };
   bf16x8_t vf[2][DB];
-  auto vbase = [&](int j) { return vslot(j >> 1) + (j & 1) * 32 * VROW + v_rd; };
   auto read_vfrag = [&](const char* vb, int half, int db) __attribute__((always_inline)) {
     const char* p = vb + half * 16 * VROW + db * 64;
     const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(DIT_LDS(i16x4_t, p));

@@ -24,7 +24,7 @@ constexpr int kMaxDevices = 64;
 // 0 = not checked yet, 1 = gfx950 and kernels configured, 2 = unsupported device
 std::atomic<int> g_device_state[kMaxDevices];
 // compute units per device (set with the device state)
-int g_num_cu[kMaxDevices];
+std::atomic<int> g_num_cu[kMaxDevices];   // published by g_device_state's release
 
 // Kernel configurations. bf16 d = 128 runs the 64-rows-per-wave pipelined
 // kernel (256 rows per workgroup); d = 64 the 32-rows-per-wave kernel with
@@ -87,7 +87,7 @@ int check_device() {
     int n_cu = 0;
     if (hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n_cu <= 0)
       return DIT_ATTN_EDEVICE;
-    g_num_cu[dev] = n_cu;
+    g_num_cu[dev].store(n_cu, std::memory_order_relaxed);
   }
   if (dev < kMaxDevices) g_device_state[dev].store(ok ? 1 : 2, std::memory_order_release);
   return ok ? DIT_ATTN_OK : DIT_ATTN_EDEVICE;
@@ -96,7 +96,8 @@ int check_device() {
 int cu_count() {
   int dev = 0;
   (void)hipGetDevice(&dev);
-  return dev >= 0 && dev < kMaxDevices && g_num_cu[dev] > 0 ? g_num_cu[dev] : 256;
+  const int n = dev >= 0 && dev < kMaxDevices ? g_num_cu[dev].load(std::memory_order_relaxed) : 0;
+  return n > 0 ? n : 256;
 }
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
