@@ -16,7 +16,10 @@ one query row, so a sample is the same computation, only fewer rows), and
 ``clocks`` are the GPU's shader and memory clocks read by a child process
 (amd-smi) before and after the timed work; ``cold`` times single calls after
 a 512 MiB scrub of the caches; ``no_workspace`` times the short entry point
-dit_attn_fwd, which runs one workgroup per query tile.
+dit_attn_fwd, which runs one workgroup per query tile; ``sustained`` is the
+rate of the timed step over the second half of about four seconds of
+back-to-back calls run after the companions (the timed ``value`` covers the
+first calls of the process, before the card's power management settles).
 ``fp8``, ``fp8_mx`` and ``blocksparse`` are companion figures of the same
 workload: the e4m3 path with per-tensor scales, the e4m3 path with one scale
 per 32 values (scaled MFMA), and block-sparse attention over the text key
@@ -372,13 +375,28 @@ def main(argv=None):
 
         th = threading.Thread(target=sample)
         th.start()
-        for _ in range(n_load):
+        # the same calls timed by events: the rate they settle at over the
+        # second half (the timed `value` above covers the first calls of the
+        # process, before the card's power management has settled)
+        half = n_load // 2
+        e0, e_mid, e_end = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+        e0.record()
+        for i in range(n_load):
+            if i == half:
+                e_mid.record()
             step()
+        e_end.record()
         torch.cuda.synchronize()
         done.set()
         th.join()
         line["clocks"] = {"idle_before": clocks_before, "under_load": [r for r in during if r["busy"]],
                           "calls_enqueued": n_load}
+        ms_first, ms_second = e0.elapsed_time(e_mid), e_mid.elapsed_time(e_end)
+        line["sustained"] = {
+            "value": round(flops * (n_load - half) / (ms_second * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
+            "first_half_value": round(flops * half / (ms_first * 1e-3) / 1e12, 2),
+            "calls": n_load, "seconds": round((ms_first + ms_second) * 1e-3, 2),
+            "kind": "back-to-back calls of the timed step after the companions; value over the second half"}
 
         def step_short():
             st = dit.dit_attn_fwd(qd, kd, vd, od, B, H, N, d, scale, dit.DIT_ATTN_BF16, handle)
